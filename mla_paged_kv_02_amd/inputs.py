@@ -1,0 +1,192 @@
+"""Seeded synthetic inputs for paged MLA decode.
+
+This module only draws random numbers and lays them out (bf16 rounding of the
+draws, the page permutation, the block table, NaN poisoning of unused cache
+rows).  It holds none of the attention arithmetic, so both the GPU path and
+the CPU oracle can be fed from it.
+
+Workloads (MLA decode over a paged latent cache with 64-token pages, as in
+"DeepSeek publica FlashMLA como codigo abierto", release bullets; sequential
+absorption bmms as in "[Attention] MLA get rid of materialization", PR
+description).  Every cache row is 576 bf16 values (512 latent + 64 rope).
+
+  tiny           batch 2, s_q 1, h_q 16, lengths {37, 130}
+  memory_bound   batch 64, s_q 1, h_q 16, lengths ~ N(4096, 1024) in [1, 8192]
+  compute_bound  batch 128, s_q 2 causal, h_q 128, lengths ~ N(4096, 1024) in [2, 8192]
+  skewed         batch 32, s_q 1, h_q 16, one length 131072 and 31 of 1024
+  full_step      batch 128, h 128, length 8192 each; q_nope [.,.,128],
+                 W_UK [128,128,512], W_UV [128,512,128] ~ N(0, 0.02)
+
+Q and the cache are N(0, 1) rounded once to bf16 (round to nearest even);
+scale = fp32(192 ** -0.5).  N(mu, sigma) takes sigma as the standard
+deviation; sampled lengths are rounded half-to-even, then clipped.
+
+Seeds: numpy SeedSequence(seed).spawn(5) gives independent streams for
+[lengths, page permutation, q, cache, weights].
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+D_QK = 576
+D_V = 512
+D_ROPE = 64
+PAGE = 64
+SCALE = float(np.float32(192.0 ** -0.5))
+BF16_NAN = 0x7FC0
+
+CONFIG_INDEX = {"tiny": 0, "memory_bound": 1, "compute_bound": 2, "skewed": 3, "full_step": 4}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even; NaN -> quiet NaN."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = BF16_NAN
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(rng: np.random.Generator, shape, std: float = 1.0,
+                chunk: int = 1 << 24) -> np.ndarray:
+    """N(0, std) draws rounded to bf16, generated in chunks to bound memory."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        v = rng.standard_normal(e - s, dtype=np.float32)
+        if std != 1.0:
+            v *= np.float32(std)
+        out[s:e] = f32_to_bf16_bits(v)
+    return out.reshape(shape)
+
+
+@dataclass
+class DecodeInputs:
+    """Host-side inputs of one decode call (bf16 tensors as uint16 bits)."""
+    q: np.ndarray             # uint16 [B, s_q, h_q, 576]
+    kv: np.ndarray            # uint16 [num_pages, 64, 576]
+    block_table: np.ndarray   # int32 [B, bt_stride]; -1 past each sequence's pages
+    seqlens: np.ndarray       # int32 [B]
+    s_q: int
+    h_q: int
+    causal: bool
+    scale: float = SCALE
+    name: str = "custom"
+    extra: dict = field(default_factory=dict)   # full_step weights etc.
+
+    @property
+    def batch(self) -> int:
+        return int(self.seqlens.shape[0])
+
+    def blocks(self) -> np.ndarray:
+        return (self.seqlens.astype(np.int64) + PAGE - 1) // PAGE
+
+
+def _lengths(name: str, rng: np.random.Generator) -> np.ndarray:
+    if name == "tiny":
+        return np.array([37, 130], dtype=np.int32)
+    if name == "memory_bound":
+        return np.clip(np.rint(rng.normal(4096.0, 1024.0, 64)), 1, 8192).astype(np.int32)
+    if name == "compute_bound":
+        return np.clip(np.rint(rng.normal(4096.0, 1024.0, 128)), 2, 8192).astype(np.int32)
+    if name == "skewed":
+        n = np.full(32, 1024, dtype=np.int32)
+        n[int(rng.integers(0, 32))] = 131072
+        return n
+    if name == "full_step":
+        return np.full(128, 8192, dtype=np.int32)
+    raise KeyError(name)
+
+
+_SHAPES = {  # name -> (s_q, h_q, causal)
+    "tiny": (1, 16, False),
+    "memory_bound": (1, 16, False),
+    "compute_bound": (2, 128, True),
+    "skewed": (1, 16, False),
+    "full_step": (1, 128, False),
+}
+
+
+def paged_cache(seqlens: np.ndarray, rng_perm: np.random.Generator,
+                rng_kv: np.random.Generator, *, extra_pages: int = 2,
+                bt_slack: int = 1, poison: bool = True, permute: bool = True,
+                page: int = PAGE, width: int = D_QK):
+    """Build a shuffled paged latent cache for the given lengths.
+
+    Logical block t of sequence b holds tokens [page*t, page*t+page); the data are
+    drawn in logical order (so a different permutation keeps the content) and
+    placed at physical page perm[first_block_of_b + t].  Rows past a
+    sequence's length and the `extra_pages` unreferenced pages are NaN when
+    `poison`.  Returns (kv uint16 [P, page, width], block_table int32 [B, S]).
+    The defaults are the real cache geometry; tests of the oracle alone may
+    shrink `page` and `width`.
+    """
+    seqlens = np.asarray(seqlens, dtype=np.int64)
+    nblk = (seqlens + page - 1) // page
+    total = int(nblk.sum())
+    num_pages = total + extra_pages
+    logical = normal_bf16(rng_kv, (total, page, width))
+    perm = rng_perm.permutation(num_pages) if permute else np.arange(num_pages)
+    kv = np.full((num_pages, page, width), BF16_NAN if poison else 0, dtype=np.uint16)
+    kv[perm[:total]] = logical
+    del logical
+    stride = int(nblk.max(initial=0)) + bt_slack
+    bt = np.full((len(seqlens), max(stride, 1)), -1, dtype=np.int32)
+    first = np.concatenate([[0], np.cumsum(nblk)[:-1]]).astype(np.int64)
+    for b in range(len(seqlens)):
+        nb = int(nblk[b])
+        bt[b, :nb] = perm[first[b]:first[b] + nb]
+        tail = int(seqlens[b] % page)
+        if poison and nb and tail:
+            kv[bt[b, nb - 1], tail:, :] = BF16_NAN
+    return kv, bt
+
+
+def make_decode(seqlens, *, s_q: int, h_q: int, causal: bool, seed: int,
+                name: str = "custom", extra_pages: int = 2, poison: bool = True,
+                permute: bool = True, bt_slack: int = 1) -> DecodeInputs:
+    """Decode inputs for explicit lengths (tests use this for edge cases)."""
+    ss = np.random.SeedSequence(seed).spawn(5)
+    rng_perm, rng_q, rng_kv = (np.random.default_rng(ss[i]) for i in (1, 2, 3))
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    kv, bt = paged_cache(seqlens, rng_perm, rng_kv, extra_pages=extra_pages,
+                         poison=poison, permute=permute, bt_slack=bt_slack)
+    q = normal_bf16(rng_q, (len(seqlens), s_q, h_q, D_QK))
+    return DecodeInputs(q=q, kv=kv, block_table=bt, seqlens=seqlens, s_q=s_q, h_q=h_q,
+                        causal=causal, name=name)
+
+
+def make_config(name: str, seed: Optional[int] = None) -> DecodeInputs:
+    """One of the five named workloads; seed defaults to 1000 + its index."""
+    if seed is None:
+        seed = 1000 + CONFIG_INDEX[name]
+    ss = np.random.SeedSequence(seed).spawn(5)
+    rng_len, rng_perm, rng_q, rng_kv, rng_w = (np.random.default_rng(s) for s in ss)
+    s_q, h_q, causal = _SHAPES[name]
+    seqlens = _lengths(name, rng_len)
+    kv, bt = paged_cache(seqlens, rng_perm, rng_kv)
+    if name == "full_step":
+        B, H = len(seqlens), h_q
+        q_nope = normal_bf16(rng_q, (B, H, 128))
+        q_rope = normal_bf16(rng_q, (B, H, D_ROPE))
+        w_uk = normal_bf16(rng_w, (H, 128, D_V), std=0.02)
+        w_uv = normal_bf16(rng_w, (H, D_V, 128), std=0.02)
+        q = np.zeros((B, 1, H, D_QK), dtype=np.uint16)
+        q[:, 0, :, D_V:] = q_rope
+        return DecodeInputs(q=q, kv=kv, block_table=bt, seqlens=seqlens, s_q=1, h_q=H,
+                            causal=False, name=name,
+                            extra=dict(q_nope=q_nope, q_rope=q_rope, w_uk=w_uk, w_uv=w_uv))
+    q = normal_bf16(rng_q, (len(seqlens), s_q, h_q, D_QK))
+    return DecodeInputs(q=q, kv=kv, block_table=bt, seqlens=seqlens, s_q=s_q, h_q=h_q,
+                        causal=causal, name=name)
+

@@ -1,0 +1,213 @@
+/*
+ * mla_oracle.c -- plain, slow fp64 CPU reference for paged MLA decode.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
+ * includes this file; only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load it.  It shares no code, header, table
+ * or helper with the GPU path.
+ *
+ * What it computes (the plain definition; no blocking, fusion or reordering):
+ *
+ *   Multi-head latent attention decode over a paged latent cache, as released
+ *   in "DeepSeek publica FlashMLA como codigo abierto" (release bullets: MLA
+ *   decoding kernel, BF16, paged KV cache with block size 64, variable
+ *   sequence lengths).  Every cached token is one latent row of d_qk bf16
+ *   values (512 compressed dims followed by 64 rope dims).  All h_q query
+ *   heads read the same row: the key is the whole row, the value is its
+ *   first d_v entries.  Token j of sequence b lives in physical page
+ *   block_table[b][j / page], row j % page.
+ *
+ *   For every sequence b, query i < s_q and head h:
+ *     L      = n_b                      (no mask)
+ *            = n_b - s_q + 1 + i        (causal: query i sits at absolute
+ *                                        position n_b - s_q + i and sees keys
+ *                                        up to and including that position)
+ *     s_j    = scale * sum_d q[b,i,h,d] * k_j[d]            for j < L
+ *     m      = max_j s_j,   w_j = exp(s_j - m),   l = sum_j w_j
+ *     out    = (sum_j w_j * k_j[0:d_v]) / l
+ *     lse    = m + ln(l)
+ *   An empty key set gives out = 0 and lse = -inf (the log of an empty sum).
+ *
+ *   Split-KV merge (used to check partial results): each contiguous key range
+ *   r of a row has its own (o_r, lse_r) from the formula above; with
+ *   M = max_r lse_r, lse = M + ln(sum_r exp(lse_r - M)) and
+ *   out = sum_r exp(lse_r - lse) * o_r.  All-empty gives out 0, lse -inf.
+ *
+ *   Absorption bmm ("[Attention] MLA get rid of materialization", PR
+ *   description: the absorbed W_Q_UK / W_UV_O products are not materialized;
+ *   the up-projections are applied as sequential batched matmuls instead):
+ *     y[b,h,n] = sum_k x[b,h,k] * W[h,k,n]
+ *
+ * Precision: inputs that are bf16 in the product (cache rows, weights) are
+ * passed as raw bf16 bit patterns and widened exactly to fp64 here;
+ * activations are passed as fp64.  All arithmetic is fp64 and nothing is
+ * rounded on the way out.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC mla_oracle.c -o liboracle.so -lm
+ * (no -ffast-math: IEEE semantics are part of the definition).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+/* Exact widening of a bf16 bit pattern: it is the top half of an fp32. */
+static double bf16_bits_to_double(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int oracle_max_threads(void) { return omp_get_max_threads(); }
+
+/* Number of keys query i of a sequence of length n may see. */
+static int64_t visible_keys(int64_t n, int s_q, int i, int causal)
+{
+    int64_t L = causal ? n - s_q + 1 + i : n;
+    return L < 0 ? 0 : L;
+}
+
+/*
+ * Attention of every (b, i, h) row over the keys j with
+ * key_begin[b] <= j < min(key_end[b], L) (L as above).  Passing NULL for
+ * key_begin / key_end means 0 / n_b, i.e. the full decode.
+ *
+ *   q           fp64 [batch][s_q][h_q][d_qk]
+ *   kv_cache    bf16 bits [num_pages][page][d_qk]
+ *   block_table int32 [batch][bt_stride]
+ *   seqlens     int32 [batch]
+ *   out         fp64 [batch][s_q][h_q][d_v]
+ *   lse         fp64 [batch][s_q][h_q]
+ *
+ * Returns 0, or -1 if a needed block-table entry is outside [0, num_pages)
+ * or a length is negative or beyond the block table (nothing is read then
+ * for that row; the caller treats any nonzero return as a failed check).
+ */
+int oracle_attend(const double *q, const uint16_t *kv_cache, int64_t num_pages,
+                  const int32_t *block_table, int64_t bt_stride,
+                  const int32_t *seqlens, int batch, int s_q, int h_q,
+                  int d_qk, int d_v, int page, float scale, int causal,
+                  const int64_t *key_begin, const int64_t *key_end,
+                  double *out, double *lse)
+{
+    const double scale64 = (double)scale;
+    const int64_t rows = (int64_t)batch * s_q * h_q;
+    int err = 0;
+
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int b = (int)(r / ((int64_t)s_q * h_q));
+        const int i = (int)((r / h_q) % s_q);
+        const int64_t n = seqlens[b];
+        const double *qrow = q + r * d_qk;
+        double *orow = out + r * d_v;
+
+        int64_t lo = key_begin ? key_begin[b] : 0;
+        int64_t hi = key_end ? key_end[b] : n;
+        const int64_t L = visible_keys(n, s_q, i, causal);
+        if (hi > L) hi = L;
+        if (lo < 0) lo = 0;
+
+        for (int e = 0; e < d_v; ++e) orow[e] = 0.0;
+        lse[r] = -INFINITY;
+        if (n < 0 || n > bt_stride * (int64_t)page) { err |= 1; continue; }
+        if (hi <= lo) continue;
+
+        /* pointers to the key rows of this row's key range */
+        const int64_t cnt = hi - lo;
+        const uint16_t **krow = (const uint16_t **)malloc((size_t)cnt * sizeof *krow);
+        double *s = (double *)malloc((size_t)cnt * sizeof *s);
+        int bad = 0;
+        for (int64_t t = 0; t < cnt; ++t) {
+            const int64_t j = lo + t;
+            const int64_t phys = block_table[(int64_t)b * bt_stride + j / page];
+            if (phys < 0 || phys >= num_pages) { bad = 1; break; }
+            krow[t] = kv_cache + (phys * page + j % page) * d_qk;
+        }
+        if (bad) { free(krow); free(s); err |= 1; continue; }
+
+        /* logits */
+        for (int64_t t = 0; t < cnt; ++t) {
+            double dot = 0.0;
+            for (int d = 0; d < d_qk; ++d)
+                dot += qrow[d] * bf16_bits_to_double(krow[t][d]);
+            s[t] = scale64 * dot;
+        }
+        /* softmax with the max subtracted, then the weighted sum of values */
+        double m = s[0];
+        for (int64_t t = 1; t < cnt; ++t)
+            if (s[t] > m) m = s[t];
+        double l = 0.0;
+        for (int64_t t = 0; t < cnt; ++t) {
+            const double w = exp(s[t] - m);
+            l += w;
+            for (int e = 0; e < d_v; ++e)
+                orow[e] += w * bf16_bits_to_double(krow[t][e]);
+        }
+        for (int e = 0; e < d_v; ++e) orow[e] /= l;
+        lse[r] = m + log(l);
+        free(krow);
+        free(s);
+    }
+    return err ? -1 : 0;
+}
+
+/*
+ * Merge n_parts partial results per row.
+ *   o_parts   fp64 [n_parts][rows][d_v]
+ *   lse_parts fp64 [n_parts][rows]      (-inf marks an empty part)
+ *   out       fp64 [rows][d_v], lse fp64 [rows]
+ */
+void oracle_combine(const double *o_parts, const double *lse_parts, int n_parts,
+                    int64_t rows, int d_v, double *out, double *lse)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double M = -INFINITY;
+        for (int p = 0; p < n_parts; ++p)
+            if (lse_parts[p * rows + r] > M) M = lse_parts[p * rows + r];
+        double *orow = out + r * d_v;
+        for (int e = 0; e < d_v; ++e) orow[e] = 0.0;
+        if (M == -INFINITY) { lse[r] = -INFINITY; continue; }
+        double total = 0.0;
+        for (int p = 0; p < n_parts; ++p)
+            total += exp(lse_parts[p * rows + r] - M);
+        const double L = M + log(total);
+        lse[r] = L;
+        for (int p = 0; p < n_parts; ++p) {
+            const double lp = lse_parts[p * rows + r];
+            if (lp == -INFINITY) continue;
+            const double w = exp(lp - L);
+            const double *op = o_parts + ((int64_t)p * rows + r) * d_v;
+            for (int e = 0; e < d_v; ++e) orow[e] += w * op[e];
+        }
+    }
+}
+
+/*
+ * Batched per-head matmul y[b,h,:] = x[b,h,:] . W[h]  (fp64).
+ *   x  fp64 [batch][heads][K]
+ *   w  bf16 bits [heads][K][N]
+ *   y  fp64 [batch][heads][N]
+ */
+void oracle_absorb_bmm(const double *x, const uint16_t *w, int batch, int heads,
+                       int K, int N, double *y)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < (int64_t)batch * heads; ++bh) {
+        const int h = (int)(bh % heads);
+        const double *xr = x + bh * K;
+        const uint16_t *wh = w + (int64_t)h * K * N;
+        double *yr = y + bh * N;
+        for (int n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k)
+                acc += xr[k] * bf16_bits_to_double(wh[(int64_t)k * N + n]);
+            yr[n] = acc;
+        }
+    }
+}
