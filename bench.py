@@ -1,0 +1,187 @@
+"""Benchmark: paged MLA decode on one MI355X.
+
+A step is one pass of the decode hot path over one batch: the split
+schedule (mla_get_metadata) and the decode with its split-KV merge
+(mla_decode).  The default workload is the memory-bound configuration
+(batch 64, s_q 1, h_q 16, lengths ~ N(4096, 1024) clipped to [1, 8192],
+shuffled 64-token pages of 576-wide bf16 latent rows).  Inputs are resident
+in HBM before timing; the cache is replicated so consecutive steps read
+different copies and no step is served from the 256 MB last-level cache
+warmed by the previous one.
+
+Prints one JSON line.  Throughput is algorithmic bytes (Q + each attended
+cache row once per sequence + out + lse) per second; TFLOP/s uses
+2 * h_q * keys * (576 + 512).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged MLA decode: achieved HBM GB/s + bf16 TFLOPS (% roofline), s_k≈4096"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+D_QK, D_V = 576, 512
+
+WORKLOADS = {
+    "memory_bound": "batch 64, s_q 1, h_q 16, d 576/512, seqlens ~N(4096,1024) clipped [1,8192], "
+                    "page 64, shuffled pages, bf16 N(0,1), scale 192^-0.5",
+    "compute_bound": "batch 128, s_q 2 causal, h_q 128, d 576/512, seqlens ~N(4096,1024) clipped "
+                     "[2,8192], page 64, shuffled pages, bf16 N(0,1), scale 192^-0.5",
+    "skewed": "batch 32, s_q 1, h_q 16, one seq of 131072 + 31 of 1024, page 64, bf16 N(0,1)",
+    "tiny": "batch 2, s_q 1, h_q 16, seqlens {37,130}, page 64",
+}
+
+
+def algorithmic_bytes(seqlens, s_q, h_q):
+    """Q + every attended cache row once per sequence + out (bf16) + lse (fp32)."""
+    seqlens = np.asarray(seqlens, dtype=np.int64)
+    rows = len(seqlens) * s_q * h_q
+    return rows * D_QK * 2 + int(seqlens.sum()) * D_QK * 2 + rows * D_V * 2 + rows * 4
+
+
+def algorithmic_flops(seqlens, s_q, h_q, causal):
+    seqlens = np.asarray(seqlens, dtype=np.int64)
+    keys = 0
+    for i in range(s_q):
+        L = seqlens - s_q + 1 + i if causal else seqlens
+        keys += int(np.clip(L, 0, None).sum())
+    return 2 * h_q * keys * (D_QK + D_V)
+
+
+def cpu_baseline(x, min_seconds: float):
+    """The fp64 oracle on the host cores, repeated over the full batch until
+    `min_seconds` of work; returns its GB/s on the same algorithmic bytes."""
+    from oracle import oracle as orc
+    threads = orc.max_threads()
+    times = []
+    t_end = time.perf_counter() + min_seconds
+    while True:
+        t0 = time.perf_counter()
+        orc.attend(x.q, x.kv, x.block_table, x.seqlens, s_q=x.s_q, h_q=x.h_q, scale=x.scale,
+                   causal=x.causal)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end or len(times) >= 200:
+            break
+    med = float(np.median(times))
+    gbs = algorithmic_bytes(x.seqlens, x.s_q, x.h_q) / med / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "full %s batch (%d sequences, fp64), median of %d repetitions, %.3f s each"
+                      % (x.name, x.batch, len(times), med)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="memory_bound", choices=sorted(WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="cache copies rotated over steps (0: enough for >= 1 GiB)")
+    ap.add_argument("--num-parts", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_paged_kv_02_amd as mla
+    from mla_paged_kv_02_amd import inputs as gen
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    x = gen.make_config(args.config)
+    kv_bytes = x.kv.nbytes
+    replicas = args.replicas or max(2, int(np.ceil((1 << 30) / kv_bytes)))
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q = to_dev(x.q)
+    kv0 = to_dev(x.kv)
+    kvs = [kv0] + [kv0.clone() for _ in range(replicas - 1)]
+    bt = torch.from_numpy(x.block_table).to(dev)
+    seqlens = torch.from_numpy(x.seqlens).to(dev)
+    parts = args.num_parts or mla.default_num_parts(x.batch, x.s_q, x.h_q, 0)
+    meta = torch.empty(mla.metadata_ints(x.batch, parts), dtype=torch.int32, device=dev)
+    ws = torch.empty(mla.workspace_bytes(x.batch, x.s_q, x.h_q, parts), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((x.batch, x.s_q, x.h_q, D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((x.batch, x.s_q, x.h_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mla.get_metadata(seqlens, x.s_q, x.h_q, parts, out=meta)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.decode(q, kvs[i % replicas], bt, seqlens, meta, parts, scale=x.scale,
+                   causal=x.causal, workspace=ws, out=out, lse=lse)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    meta_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+
+    nbytes = algorithmic_bytes(x.seqlens, x.s_q, x.h_q)
+    flops = algorithmic_flops(x.seqlens, x.s_q, x.h_q, x.causal)
+    value = nbytes / (ms_step / 1e3) / 1e9
+    achieved = nbytes / (decode_ms / 1e3) / 1e9
+    tflops = flops / (decode_ms / 1e3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 cache and queries, shuffled pages)",
+        "config": {"workload": "%s: %s" % (args.config, WORKLOADS[args.config]),
+                   "global_batch": x.batch, "seq_len": int(round(float(x.seqlens.mean()))),
+                   "s_q": x.s_q, "h_q": x.h_q, "num_parts": parts, "cache_replicas": replicas,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "mla_decode (decode_r16_kernel + combine_kernel), HIP events",
+                     "ms": round(decode_ms, 5)},
+        "tflops": round(tflops, 3),
+        "tflops_frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "metadata_ms": round(meta_ms, 5),
+        "algorithmic_bytes": nbytes,
+        "algorithmic_flops": flops,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

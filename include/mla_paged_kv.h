@@ -1,0 +1,173 @@
+/*
+ * mla_paged_kv.h -- C ABI of libmla_paged_kv.so: multi-head latent attention
+ * (MLA) decode over a paged latent KV cache on AMD MI355X (gfx950).
+ *
+ * The operation is the MLA decode kernel released as FlashMLA ("DeepSeek
+ * publica FlashMLA como codigo abierto", release bullets): BF16, a paged KV
+ * cache with 64-token blocks, variable-length sequences, forward only.  The
+ * query up-projection and value down-projection are applied as sequential
+ * batched matmuls rather than materialized absorbed weights ("[Attention] MLA
+ * get rid of materialization", PR description).
+ *
+ * Conventions shared by every call
+ *   - bf16 tensors are passed as their raw 16-bit patterns (uint16_t).
+ *   - Pointers marked [device] must be device memory of the current HIP
+ *     device; [host] pointers are ordinary host memory.  The caller owns all
+ *     buffers; the library keeps no pointer after a call returns and
+ *     allocates no device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call that
+ *     launches work only enqueues it on that stream and returns without
+ *     synchronizing; results are ready once the stream reaches that point.
+ *   - Every call returns an mla_status.  Arguments are validated on the host
+ *     before anything is launched; on an error nothing is enqueued and
+ *     mla_last_error() holds a one-line reason (per calling thread).  No
+ *     call aborts or throws.
+ *   - The contents of device buffers (sequence lengths, block-table entries)
+ *     are trusted: every length must satisfy 0 <= n_b <= bt_stride * 64 and
+ *     every block-table entry a sequence uses must lie in [0, num_pages).
+ *     Entries past ceil(n_b / 64) are never read.
+ *
+ * Geometry (fixed by the model; other values return MLA_ERR_UNSUPPORTED)
+ *   d_qk = 576: each cached token is one latent row of 512 compressed dims
+ *               followed by 64 rope dims; keys are the whole row.
+ *   d_v  = 512: values are the first 512 dims of the same row.
+ *   page = 64 tokens; kv_cache is [num_pages][64][576] bf16, a page is
+ *          73,728 contiguous bytes.
+ *   Rows of a sequence: R = s_q * h_q, ordered (query i, head h) -> i*h_q+h.
+ *   h_q must be 16, 32, 64 or 128; 1 <= s_q <= 16.
+ */
+#ifndef MLA_PAGED_KV_H
+#define MLA_PAGED_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad stride   */
+    MLA_ERR_UNSUPPORTED = 2, /* shape outside the supported geometry      */
+    MLA_ERR_WORKSPACE = 3,   /* workspace pointer null or too small       */
+    MLA_ERR_HIP = 4          /* a HIP runtime call or launch failed       */
+} mla_status;
+
+/* Static name of a status code (never NULL). */
+const char *mla_status_str(int status);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char *mla_last_error(void);
+
+/* Number of compute units of HIP device `device` -> *cus [host]. */
+int mla_device_cus(int device, int *cus);
+
+/* Scheduler parts for a shape: how many key ranges the sequences are cut
+ * into (one workgroup per part and 16-row tile).  Pure host arithmetic. */
+int mla_default_num_parts(int num_cus, int batch, int s_q, int h_q);
+
+/* int32 count of the metadata buffer for (batch, num_parts):
+ *   8 * num_parts      part records {seq_begin, tok_begin, seq_end, tok_end,
+ *                      slot_begin, 0, 0, 0}: the part covers tokens
+ *                      [tok_begin, ...) of sequence seq_begin, every token of
+ *                      the sequences strictly between, and [0, tok_end) of
+ *                      seq_end (or [tok_begin, tok_end) when they are equal);
+ *                      seq_begin = -1 marks an empty part.  slot_begin is the
+ *                      partial-result slot of its first sequence.
+ *   batch + 1          split_offsets: sequence b owns partial slots
+ *                      [split_offsets[b], split_offsets[b+1]); a sequence
+ *                      with exactly one slot is written in place.
+ *   1                  total chunks (16-token units) over the batch. */
+size_t mla_metadata_ints(int batch, int num_parts);
+
+/* Bytes of decode workspace: fp32 partial outputs and log-sum-exps for up
+ * to batch + num_parts splits of R rows:
+ *   (batch + num_parts) * s_q * h_q * (512 + 1) * 4. */
+size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts);
+
+/*
+ * Variable-length split scheduling (the FlashMLA release bullets name
+ * serving batches of sequences of differing lengths as its target).  Reads
+ * the sequence lengths on the
+ * device (no host synchronization), cuts the flattened list of 16-token
+ * chunks of all sequences into `num_parts` contiguous ranges whose sizes
+ * differ by at most one chunk, and writes the metadata described above.
+ * Compute once per decode step; it stays valid for every layer while the
+ * lengths do not change.
+ *   seqlens  [device] int32 [batch], each >= 0
+ *   metadata [device] int32 [mla_metadata_ints(batch, num_parts)] (output)
+ *   1 <= batch <= 16384, 1 <= num_parts <= 65536.
+ */
+int mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int num_parts,
+                     int32_t *metadata, void *stream);
+
+/*
+ * Paged MLA decode.  For every sequence b, query i and head h, with
+ * n = seqlens[b] and L = n (causal = 0) or L = n - s_q + 1 + i (causal = 1:
+ * query i sits at absolute position n - s_q + i):
+ *   s_j = scale * <q[b,i,h,:], kv_row(b, j)>         for j < L
+ *   out[b,i,h,:] = sum_j softmax(s)_j * kv_row(b, j)[0:512]
+ *   lse[b,i,h]   = ln sum_j exp(s_j)                   (natural log)
+ * where kv_row(b, j) = kv_cache[block_table[b*bt_stride + j/64]][j%64][:].
+ * A row with L <= 0 gets out = 0 and lse = -inf.  Softmax runs in fp32 on
+ * bf16 MFMA products; out is rounded to bf16 (nearest even).
+ *
+ *   q           [device] bf16 [batch][s_q][h_q][576]
+ *   kv_cache    [device] bf16 [num_pages][64][576]
+ *   block_table [device] int32 [batch][bt_stride]
+ *   seqlens     [device] int32 [batch]
+ *   metadata    [device] from mla_get_metadata with the same batch, s_q, h_q,
+ *               num_parts and lengths
+ *   workspace   [device] >= mla_workspace_bytes(batch, s_q, h_q, num_parts)
+ *   out         [device] bf16 [batch][s_q][h_q][512]
+ *   lse         [device] fp32 [batch][s_q][h_q]
+ * Sequences cut into several parts are merged by the combine kernel on the
+ * same stream before the call's work completes.
+ */
+int mla_decode(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
+               const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens,
+               int batch, int s_q, int h_q, int d_qk, int d_v, int page_size,
+               float scale, int causal, const int32_t *metadata, int num_parts,
+               void *workspace, size_t workspace_bytes, uint16_t *out, float *lse,
+               void *stream);
+
+/*
+ * Split-KV merge.  Sequence b's partial results are slots
+ * [split_offsets[b], split_offsets[b+1]) of o_part / lse_part; each slot
+ * holds a normalized partial output and its natural-log lse over a disjoint
+ * key range (lse = -inf marks an empty range).  With M = max_s lse_s:
+ *   lse = M + ln sum_s exp(lse_s - M),  out = sum_s exp(lse_s - lse) * o_s.
+ * A sequence with no slot, or whose slots are all empty, gets out = 0 and
+ * lse = -inf.
+ *   o_part        [device] fp32 [total_slots][s_q*h_q][512]
+ *   lse_part      [device] fp32 [total_slots][s_q*h_q]
+ *   split_offsets [device] int32 [batch + 1], nondecreasing, from 0
+ *   out           [device] bf16 [batch][s_q][h_q][512]
+ *   lse           [device] fp32 [batch][s_q][h_q]
+ */
+int mla_combine(const float *o_part, const float *lse_part, const int32_t *split_offsets,
+                int batch, int s_q, int h_q, int d_v, uint16_t *out, float *lse, void *stream);
+
+/*
+ * Per-head batched matmul for the non-materialized absorption ("[Attention]
+ * MLA get rid of materialization", PR description):
+ *   y[b, h, n] = sum_k x[b, h, k] * w[h, k, n]      (fp32 accumulate, bf16 out)
+ * Used as q_lat = q_nope . W_UK (K = 128, N = 512, writing into the first 512
+ * columns of the decode query) and as y = o_lat . W_UV (K = 512, N = 128).
+ *   x [device] bf16, element (b, h, k) at x[b*x_stride_b + h*x_stride_h + k]
+ *   w [device] bf16 [heads][K][N], contiguous
+ *   y [device] bf16, element (b, h, n) at y[b*y_stride_b + h*y_stride_h + n]
+ * K must be a positive multiple of 32 and N of 64; strides are in elements
+ * and must keep every row 16-byte aligned (multiples of 8).
+ */
+int mla_absorb_bmm(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h,
+                   const uint16_t *w, int heads, int K, int N,
+                   uint16_t *y, int64_t y_stride_b, int64_t y_stride_h, int batch,
+                   void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PAGED_KV_H */

@@ -1,0 +1,12 @@
+"""Multi-head latent attention decode over a paged latent KV cache for AMD
+MI355X (gfx950): a C-ABI library of hand-written HIP kernels
+(libmla_paged_kv.so, see include/mla_paged_kv.h) and a thin torch binding.
+
+    meta, parts = get_metadata(seqlens, s_q, h_q)
+    out, lse = decode(q, kv_cache, block_table, seqlens, meta, parts, scale=s)
+"""
+from .api import (absorb_bmm, combine, decode, default_num_parts, device_cus, get_metadata,
+                  metadata_ints, split_offsets, workspace_bytes)
+
+__all__ = ["absorb_bmm", "combine", "decode", "default_num_parts", "device_cus", "get_metadata",
+           "metadata_ints", "split_offsets", "workspace_bytes"]

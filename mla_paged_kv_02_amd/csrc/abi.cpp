@@ -1,0 +1,245 @@
+// abi.cpp -- the extern "C" entry points of libmla_paged_kv.so.
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, so argument errors are reported without a device.  Work is
+// only enqueued on the caller's stream; nothing here synchronizes, allocates
+// device memory or keeps a pointer past the call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/mla_paged_kv.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok()
+{
+    g_last_error[0] = '\0';
+    return MLA_OK;
+}
+
+int hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_heads(int h_q) { return h_q == 16 || h_q == 32 || h_q == 64 || h_q == 128; }
+
+constexpr int kMaxSq = 16;
+
+int check_rows(int batch, int s_q, int h_q)
+{
+    if (batch < 1) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+    if (s_q < 1 || s_q > kMaxSq)
+        return fail(MLA_ERR_UNSUPPORTED, "s_q must be in [1, %d] (got %d)", kMaxSq, s_q);
+    if (!supported_heads(h_q))
+        return fail(MLA_ERR_UNSUPPORTED, "h_q must be 16, 32, 64 or 128 (got %d)", h_q);
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mla_status_str(int status)
+{
+    switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    default: return "MLA_ERR_UNKNOWN";
+    }
+}
+
+const char *mla_last_error(void) { return g_last_error; }
+
+int mla_device_cus(int device, int *cus)
+{
+    if (cus == nullptr) return fail(MLA_ERR_INVALID_ARG, "cus is null");
+    int v = 0;
+    hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return hip_status(e, "hipDeviceGetAttribute");
+    *cus = v;
+    return ok();
+}
+
+int mla_default_num_parts(int num_cus, int batch, int s_q, int h_q)
+{
+    (void)batch;
+    if (num_cus < 1) num_cus = 1;
+    const int row_tiles = (s_q > 0 && h_q > 0) ? (s_q * h_q + 15) / 16 : 1;
+    int parts = num_cus / row_tiles;
+    if (parts < 1) parts = 1;
+    if (parts > mla::kMaxParts) parts = mla::kMaxParts;
+    return parts;
+}
+
+size_t mla_metadata_ints(int batch, int num_parts)
+{
+    if (batch < 0 || num_parts < 0) return 0;
+    return (size_t)mla::kPartInts * (size_t)num_parts + (size_t)batch + 2;
+}
+
+size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts)
+{
+    if (batch < 0 || s_q < 0 || h_q < 0 || num_parts < 0) return 0;
+    return ((size_t)batch + (size_t)num_parts) * (size_t)s_q * (size_t)h_q * (512 + 1) * 4;
+}
+
+int mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int num_parts,
+                     int32_t *metadata, void *stream)
+{
+    if (seqlens == nullptr || metadata == nullptr)
+        return fail(MLA_ERR_INVALID_ARG, "seqlens and metadata must be non-null");
+    if (int st = check_rows(batch, s_q, h_q)) return st;
+    if (batch > mla::kMetaMaxBatch)
+        return fail(MLA_ERR_UNSUPPORTED, "batch must be <= %d (got %d)", mla::kMetaMaxBatch, batch);
+    if (num_parts < 1 || num_parts > mla::kMaxParts)
+        return fail(MLA_ERR_INVALID_ARG, "num_parts must be in [1, %d] (got %d)", mla::kMaxParts,
+                    num_parts);
+    return hip_status(mla::launch_metadata(seqlens, batch, num_parts, metadata,
+                                           static_cast<hipStream_t>(stream)),
+                      "metadata kernel launch");
+}
+
+int mla_decode(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
+               const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens,
+               int batch, int s_q, int h_q, int d_qk, int d_v, int page_size,
+               float scale, int causal, const int32_t *metadata, int num_parts,
+               void *workspace, size_t workspace_bytes, uint16_t *out, float *lse,
+               void *stream)
+{
+    if (!q || !kv_cache || !block_table || !seqlens || !metadata || !out || !lse)
+        return fail(MLA_ERR_INVALID_ARG, "q, kv_cache, block_table, seqlens, metadata, out and "
+                                         "lse must be non-null");
+    if (int st = check_rows(batch, s_q, h_q)) return st;
+    if (batch > mla::kMetaMaxBatch)
+        return fail(MLA_ERR_UNSUPPORTED, "batch must be <= %d (got %d)", mla::kMetaMaxBatch, batch);
+    if (d_qk != 576 || d_v != 512)
+        return fail(MLA_ERR_UNSUPPORTED, "d_qk must be 576 and d_v 512 (got %d, %d)", d_qk, d_v);
+    if (page_size != 64)
+        return fail(MLA_ERR_UNSUPPORTED, "page_size must be 64 (got %d)", page_size);
+    if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1");
+    if (bt_stride < 1) return fail(MLA_ERR_INVALID_ARG, "bt_stride must be >= 1");
+    if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
+    if (num_parts < 1 || num_parts > mla::kMaxParts)
+        return fail(MLA_ERR_INVALID_ARG, "num_parts must be in [1, %d] (got %d)", mla::kMaxParts,
+                    num_parts);
+    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+        !aligned(block_table, 4) || !aligned(seqlens, 4) || !aligned(metadata, 4))
+        return fail(MLA_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
+    const size_t need = mla_workspace_bytes(batch, s_q, h_q, num_parts);
+    if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
+        return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu",
+                    need, workspace == nullptr ? (size_t)0 : workspace_bytes);
+
+    const int rows = s_q * h_q;
+    const size_t slots = (size_t)batch + (size_t)num_parts;
+    float *o_part = static_cast<float *>(workspace);
+    float *lse_part = o_part + slots * (size_t)rows * 512;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    mla::DecodeParams p;
+    p.q = q;
+    p.kv = kv_cache;
+    p.block_table = block_table;
+    p.bt_stride = bt_stride;
+    p.seqlens = seqlens;
+    p.meta = metadata;
+    p.num_parts = num_parts;
+    p.s_q = s_q;
+    p.h_q = h_q;
+    p.causal = causal;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.o_part = o_part;
+    p.lse_part = lse_part;
+    p.out = out;
+    p.lse = lse;
+    if (hipError_t e = mla::launch_decode_r16(p, num_parts, rows / 16, st))
+        return hip_status(e, "decode kernel launch");
+
+    mla::CombineParams c;
+    c.o_part = o_part;
+    c.lse_part = lse_part;
+    c.split_off = metadata + (size_t)mla::kPartInts * num_parts;
+    c.rows = rows;
+    c.skip_single = 1;
+    c.out = out;
+    c.lse = lse;
+    return hip_status(mla::launch_combine(c, batch, st), "combine kernel launch");
+}
+
+int mla_combine(const float *o_part, const float *lse_part, const int32_t *split_offsets,
+                int batch, int s_q, int h_q, int d_v, uint16_t *out, float *lse, void *stream)
+{
+    if (!o_part || !lse_part || !split_offsets || !out || !lse)
+        return fail(MLA_ERR_INVALID_ARG, "all pointers must be non-null");
+    if (int st = check_rows(batch, s_q, h_q)) return st;
+    if (d_v != 512) return fail(MLA_ERR_UNSUPPORTED, "d_v must be 512 (got %d)", d_v);
+    if (!aligned(o_part, 16) || !aligned(out, 16))
+        return fail(MLA_ERR_INVALID_ARG, "o_part and out must be 16-byte aligned");
+    mla::CombineParams c;
+    c.o_part = o_part;
+    c.lse_part = lse_part;
+    c.split_off = split_offsets;
+    c.rows = s_q * h_q;
+    c.skip_single = 0;
+    c.out = out;
+    c.lse = lse;
+    return hip_status(mla::launch_combine(c, batch, static_cast<hipStream_t>(stream)),
+                      "combine kernel launch");
+}
+
+int mla_absorb_bmm(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h,
+                   const uint16_t *w, int heads, int K, int N,
+                   uint16_t *y, int64_t y_stride_b, int64_t y_stride_h, int batch,
+                   void *stream)
+{
+    if (!x || !w || !y) return fail(MLA_ERR_INVALID_ARG, "x, w and y must be non-null");
+    if (batch < 1 || heads < 1) return fail(MLA_ERR_INVALID_ARG, "batch and heads must be >= 1");
+    if (K < 32 || K % 32 != 0 || N < 64 || N % 64 != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "K must be a multiple of 32 and N of 64 (got %d, %d)", K,
+                    N);
+    if (heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "heads must be <= 65535");
+    if (x_stride_b % 8 || x_stride_h % 8 || y_stride_b % 8 || y_stride_h % 8 ||
+        x_stride_b < 0 || x_stride_h < 0 || y_stride_b < 0 || y_stride_h < 0)
+        return fail(MLA_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements");
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16))
+        return fail(MLA_ERR_INVALID_ARG, "x, w and y must be 16-byte aligned");
+    mla::AbsorbParams p;
+    p.x = x;
+    p.x_sb = x_stride_b;
+    p.x_sh = x_stride_h;
+    p.w = w;
+    p.K = K;
+    p.N = N;
+    p.y = y;
+    p.y_sb = y_stride_b;
+    p.y_sh = y_stride_h;
+    p.batch = batch;
+    return hip_status(mla::launch_absorb(p, heads, static_cast<hipStream_t>(stream)),
+                      "absorb kernel launch");
+}
+
+}  // extern "C"

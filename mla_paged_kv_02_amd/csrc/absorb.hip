@@ -1,0 +1,95 @@
+// absorb.hip -- per-head batched matmul for non-materialized MLA absorption.
+//
+// "[Attention] MLA get rid of materialization" (PR description) keeps W_UK
+// and W_UV separate and applies them as sequential matmuls around the latent
+// attention: q_lat = q_nope . W_UK[h] before it, y = o_lat . W_UV[h] after it.
+// Each is y[b, h, :] = x[b, h, :] . W[h] with W[h] a K x N bf16 matrix.
+//
+// gfx950 mapping: a workgroup computes a 64 (batch) x 64 (columns) tile of
+// one head as y^T = W^T x^T on v_mfma_f32_16x16x32_bf16.  W's K x 64 column
+// slab streams through LDS 32 rows at a time and is read back transposed
+// with ds_read_b64_tr_b16 (the A operand needs 8 consecutive k per lane,
+// which are 2N bytes apart in memory); x rows are already k-contiguous and
+// feed the B operand straight from global memory.  The accumulator layout
+// puts 4 consecutive output columns in each lane, so stores are 8 bytes.
+#include "mla_device.h"
+#include "kernels.h"
+
+namespace mla {
+
+constexpr int kAbsThreads = 256;
+constexpr int kAbsBM = 64;              // batch rows per workgroup (16 per wave)
+constexpr int kAbsBN = 64;              // output columns per workgroup
+constexpr int kAbsKSlab = 32;           // k rows staged per step
+constexpr int kWStride = kAbsBN + 8;    // bf16 per staged row (144 B)
+
+
+__global__ __launch_bounds__(kAbsThreads) void absorb_kernel(AbsorbParams p)
+{
+    __shared__ __attribute__((aligned(16))) short wt[kAbsKSlab * kWStride];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
+    const int n0 = blockIdx.x * kAbsBN;
+    const int m0 = blockIdx.y * kAbsBM;
+    const int h = blockIdx.z;
+
+    const uint16_t *wh = p.w + (int64_t)h * p.K * p.N;
+    const int brow = m0 + wave * 16 + r16;               // batch row of this lane (B operand)
+    const bool row_ok = brow < p.batch;
+    const uint16_t *xrow = p.x + (int64_t)(row_ok ? brow : 0) * p.x_sb + (int64_t)h * p.x_sh;
+
+    // staging: thread t copies 16 bytes: slab row t / 8, columns 8 * (t % 8)
+    const int srow = threadIdx.x >> 3;
+    const int scol = 8 * (threadIdx.x & 7);
+
+    f32x4_t acc[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // transposed-read address: lane 16g + 4e + c -> slab row 8g + e, column 4c
+    const int tr_row = 8 * g + (r16 >> 2);
+    const int tr_col = 4 * (r16 & 3);
+
+    for (int k0 = 0; k0 < p.K; k0 += kAbsKSlab) {
+        const u32x4_t wv =
+            *reinterpret_cast<const u32x4_t *>(wh + (int64_t)(k0 + srow) * p.N + n0 + scol);
+        u32x4_t xv = {0u, 0u, 0u, 0u};
+        if (row_ok) xv = *reinterpret_cast<const u32x4_t *>(xrow + k0 + 8 * g);
+        __syncthreads();   // previous slab fully consumed
+        *reinterpret_cast<u32x4_t *>(wt + srow * kWStride + scol) = wv;
+        __syncthreads();
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const short *base = wt + tr_row * kWStride + 16 * mb + tr_col;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (i16x4_t __attribute__((address_space(3))) *)(base));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (i16x4_t __attribute__((address_space(3))) *)(base + 4 * kWStride));
+            const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                              __builtin_bit_cast(bf16x8_t, xv),
+                                                              acc[mb], 0, 0, 0);
+        }
+    }
+
+    if (!row_ok) return;
+    uint16_t *yrow = p.y + (int64_t)brow * p.y_sb + (int64_t)h * p.y_sh + n0;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        u32x2_t v;
+        v[0] = pack_bf16x2(acc[mb][0], acc[mb][1]);
+        v[1] = pack_bf16x2(acc[mb][2], acc[mb][3]);
+        *reinterpret_cast<u32x2_t *>(yrow + 16 * mb + 4 * g) = v;
+    }
+}
+
+hipError_t launch_absorb(const AbsorbParams &p, int heads, hipStream_t stream)
+{
+    dim3 grid(p.N / kAbsBN, (p.batch + kAbsBM - 1) / kAbsBM, heads);
+    hipLaunchKernelGGL(absorb_kernel, grid, dim3(kAbsThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace mla

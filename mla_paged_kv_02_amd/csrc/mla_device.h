@@ -1,0 +1,62 @@
+// mla_device.h -- internal types and helpers shared by the gfx950 kernels of
+// libmla_paged_kv.so (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Cache geometry: one latent row per token, 512 compressed + 64 rope dims,
+// 64-token pages.
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kPage = 64;
+constexpr int kChunk = 16;                       // scheduling unit, tokens
+constexpr int kRowBytes = kDqk * 2;              // 1152
+constexpr int kPageBytes = kPage * kRowBytes;    // 73728
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+typedef short __attribute__((address_space(3))) lds_short_t;
+
+// gfx9 buffer descriptor word 3: 32-bit data format, no swizzle.  Reads at
+// an offset >= num_records return zero.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) r = u | 0x00400000u;   // quiet NaN
+    return r >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace mla

@@ -1,0 +1,91 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any launch (no GPU needed).
+
+Every call below fails validation by construction; none reaches a launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_paged_kv_02_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "mla_paged_kv.h")
+FAKE = 0x10000   # aligned non-null address; never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), "missing export " + n
+    assert set(names) == set(_lib.SYMBOLS)
+
+
+def test_status_strings(lib):
+    assert _lib.status_str(0) == "MLA_OK"
+    assert _lib.status_str(3) == "MLA_ERR_WORKSPACE"
+    assert _lib.status_str(99) == "MLA_ERR_UNKNOWN"
+
+
+def test_sizes(lib):
+    assert lib.mla_metadata_ints(64, 256) == 8 * 256 + 64 + 2
+    assert lib.mla_workspace_bytes(64, 1, 16, 256) == (64 + 256) * 16 * 513 * 4
+    assert lib.mla_default_num_parts(256, 64, 1, 16) == 256
+    assert lib.mla_default_num_parts(256, 128, 2, 128) == 16
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, kv=FAKE, num_pages=10, bt=FAKE, bt_stride=4, seqlens=FAKE, batch=2, s_q=1,
+             h_q=16, d_qk=576, d_v=512, page=64, scale=0.07, causal=0, meta=FAKE, parts=4,
+             ws=FAKE, ws_bytes=0, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.mla_decode(a["q"], a["kv"], a["num_pages"], a["bt"], a["bt_stride"], a["seqlens"],
+                          a["batch"], a["s_q"], a["h_q"], a["d_qk"], a["d_v"], a["page"],
+                          a["scale"], a["causal"], a["meta"], a["parts"], a["ws"], a["ws_bytes"],
+                          a["out"], a["lse"], None)
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, q=None) == _lib.MLA_ERR_INVALID_ARG
+    assert "non-null" in _lib.last_error()
+    assert _decode(lib, h_q=8) == _lib.MLA_ERR_UNSUPPORTED
+    assert _decode(lib, d_qk=512) == _lib.MLA_ERR_UNSUPPORTED
+    assert _decode(lib, page=16) == _lib.MLA_ERR_UNSUPPORTED
+    assert _decode(lib, s_q=0) == _lib.MLA_ERR_UNSUPPORTED
+    assert _decode(lib, batch=0) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(lib, causal=2) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(lib, scale=float("nan")) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(lib, parts=0) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(lib, q=FAKE + 2) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(lib, ws_bytes=100) == _lib.MLA_ERR_WORKSPACE
+    assert "workspace needs" in _lib.last_error()
+    assert _decode(lib, ws=None, ws_bytes=1 << 30) == _lib.MLA_ERR_WORKSPACE
+
+
+def test_other_validation(lib):
+    assert lib.mla_get_metadata(None, 2, 1, 16, 4, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_get_metadata(FAKE, 20000, 1, 16, 4, FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_get_metadata(FAKE, 2, 1, 16, 0, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine(FAKE, FAKE, FAKE, 2, 1, 16, 256, FAKE, FAKE, None) == \
+        _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_combine(None, FAKE, FAKE, 2, 1, 16, 512, FAKE, FAKE, None) == \
+        _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_bmm(FAKE, 0, 0, FAKE, 4, 100, 64, FAKE, 0, 0, 2, None) == \
+        _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_absorb_bmm(FAKE, 3, 0, FAKE, 4, 128, 64, FAKE, 0, 0, 2, None) == \
+        _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_device_cus(0, None) == _lib.MLA_ERR_INVALID_ARG
