@@ -21,21 +21,30 @@ namespace mla {
 
 constexpr int kMetaThreads = 1024;
 
-__device__ int block_exclusive_scan(int v, int *scratch, int &total)
+// Exclusive scan over the workgroup: shuffle scan inside each wave, then
+// every thread adds the totals of the waves before it (two barriers).
+__device__ int block_exclusive_scan(int v, int *wave_tot, int &total)
 {
-    const int t = threadIdx.x;
-    scratch[t] = v;
-    __syncthreads();
-    for (int off = 1; off < kMetaThreads; off <<= 1) {
-        const int add = t >= off ? scratch[t - off] : 0;
-        __syncthreads();
-        scratch[t] += add;
-        __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int up = __shfl_up(inc, off);
+        if (lane >= off) inc += up;
     }
-    total = scratch[kMetaThreads - 1];
-    const int excl = scratch[t] - v;
+    if (lane == 63) wave_tot[wave] = inc;
     __syncthreads();
-    return excl;
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kMetaThreads / 64; ++w) {
+        const int tw = wave_tot[w];
+        if (w < wave) before += tw;
+        total += tw;
+    }
+    __syncthreads();   // wave_tot may be rewritten by the next scan
+    return before + inc - v;
 }
 
 __device__ __forceinline__ int part_of_chunk(int64_t f, int64_t parts, int64_t total)
@@ -60,7 +69,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *s
 {
     __shared__ int prefix[kMetaMaxBatch + 1];   // chunk offsets of the sequences
     __shared__ int splits[kMetaMaxBatch + 1];   // partial-slot offsets
-    __shared__ int scratch[kMetaThreads];
+    __shared__ int scratch[kMetaThreads / 64];
     const int t = threadIdx.x;
     const int per = (batch + kMetaThreads - 1) / kMetaThreads;
     const int b0 = min(batch, t * per);

@@ -88,6 +88,25 @@ def test_page_permutation_is_bitwise_invariant():
     assert torch.equal(lse1, lse2)
 
 
+def test_metadata_reused_across_calls():
+    """One schedule serves several decode calls (as across layers)."""
+    x = gen.make_decode([900, 3000, 65, 0, 4097], s_q=2, h_q=32, causal=True, seed=21)
+    d = gu.DeviceInputs(x)
+    meta, parts = mla.get_metadata(d.seqlens, x.s_q, x.h_q, 96)
+    rng = np.random.default_rng(4)
+    for layer in range(3):
+        qb = gen.normal_bf16(rng, x.q.shape)
+        out, lse = mla.decode(gu.bits_to_dev(qb), d.kv, d.bt, d.seqlens, meta, parts,
+                              scale=x.scale, causal=True)
+        torch.cuda.synchronize()
+        x.q = qb
+        ro, rl = gu.oracle_decode(x)
+        gu.compare(gu.dev_to_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl,
+                   "layer %d" % layer)
+    m = meta.cpu().numpy()
+    assert np.array_equal(m, sc.expected_metadata(x.seqlens, parts))
+
+
 def test_repeat_runs_are_bitwise_identical():
     x = gen.make_config("memory_bound", seed=77)
     d = gu.DeviceInputs(x)
