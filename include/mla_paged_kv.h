@@ -64,7 +64,9 @@ const char *mla_last_error(void);
 int mla_device_cus(int device, int *cus);
 
 /* Scheduler parts for a shape: how many key ranges the sequences are cut
- * into (one workgroup per part and 16-row tile).  Pure host arithmetic. */
+ * into so that one workgroup per part and row tile fills the device once.
+ * A row tile is 128 query rows when s_q * h_q is a multiple of 128 (the
+ * MFMA-dense kernel), else 16 rows.  Pure host arithmetic. */
 int mla_default_num_parts(int num_cus, int batch, int s_q, int h_q);
 
 /* int32 count of the metadata buffer for (batch, num_parts):

@@ -87,7 +87,8 @@ int mla_default_num_parts(int num_cus, int batch, int s_q, int h_q)
 {
     (void)batch;
     if (num_cus < 1) num_cus = 1;
-    const int row_tiles = (s_q > 0 && h_q > 0) ? (s_q * h_q + 15) / 16 : 1;
+    const int rows = (s_q > 0 && h_q > 0) ? s_q * h_q : 16;
+    const int row_tiles = rows % mla::kWideRows == 0 ? rows / mla::kWideRows : (rows + 15) / 16;
     int parts = num_cus / row_tiles;
     if (parts < 1) parts = 1;
     if (parts > mla::kMaxParts) parts = mla::kMaxParts;
@@ -176,8 +177,11 @@ int mla_decode(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
     p.lse_part = lse_part;
     p.out = out;
     p.lse = lse;
-    if (hipError_t e = mla::launch_decode_r16(p, num_parts, rows / 16, st))
-        return hip_status(e, "decode kernel launch");
+    // 128-row tiles when the rows allow (MFMA-dense), else 16-row tiles
+    const hipError_t e = rows % mla::kWideRows == 0
+                             ? mla::launch_decode_wide(p, num_parts, rows / mla::kWideRows, st)
+                             : mla::launch_decode_r16(p, num_parts, rows / 16, st);
+    if (e != hipSuccess) return hip_status(e, "decode kernel launch");
 
     mla::CombineParams c;
     c.o_part = o_part;

@@ -53,6 +53,11 @@ hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int
                            hipStream_t stream);
 hipError_t launch_decode_r16(const DecodeParams &p, int num_parts, int row_tiles,
                              hipStream_t stream);
+// query rows per workgroup of the wide decode kernel (used when s_q*h_q is a
+// multiple of it)
+constexpr int kWideRows = 128;
+hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tiles,
+                              hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, int batch, hipStream_t stream);
 hipError_t launch_absorb(const AbsorbParams &p, int heads, hipStream_t stream);
 

@@ -45,9 +45,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
     return r >> 16;
 }
 
+// two fp32 values to packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }

@@ -45,7 +45,9 @@ def test_sizes(lib):
     assert lib.mla_metadata_ints(64, 256) == 8 * 256 + 64 + 2
     assert lib.mla_workspace_bytes(64, 1, 16, 256) == (64 + 256) * 16 * 513 * 4
     assert lib.mla_default_num_parts(256, 64, 1, 16) == 256
-    assert lib.mla_default_num_parts(256, 128, 2, 128) == 16
+    assert lib.mla_default_num_parts(256, 128, 2, 128) == 128   # two 128-row tiles
+    assert lib.mla_default_num_parts(256, 8, 1, 128) == 256     # one 128-row tile
+    assert lib.mla_default_num_parts(256, 8, 3, 32) == 42       # six 16-row tiles
 
 
 def _decode(lib, **kw):

@@ -158,3 +158,35 @@ def test_combine_entry_point():
     torch.cuda.synchronize()
     ro, rl = gu.oracle_decode(x)
     gu.compare(gu.dev_to_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl, "combine")
+
+
+@pytest.mark.parametrize("num_parts", [1, 3, 7, 64, 300])
+def test_forced_part_counts_wide_rows(num_parts):
+    """128-row tiles (s_q * h_q = 128) under many part counts: split points
+    fall inside 32-token tiles and inside pages."""
+    x = gen.make_decode([700, 3000, 65, 1, 4097, 0, 33], s_q=1, h_q=128, causal=False, seed=31)
+    _, meta, parts = _check(x, num_parts=num_parts, what="wide parts=%d" % num_parts)
+    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts))
+
+
+@pytest.mark.parametrize("s_q,h_q", [(2, 64), (4, 32), (8, 16), (2, 128)])
+def test_causal_multi_query_wide_rows(s_q, h_q):
+    x = gen.make_decode([1, 2, 5, 31, 32, 33, 64, 97, 1000, 2049], s_q=s_q, h_q=h_q, causal=True,
+                        seed=40 + s_q)
+    _check(x, what="causal wide s_q=%d h_q=%d" % (s_q, h_q))
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_scores_growing_after_first_key(h_q):
+    """The first visible key scores far below a later one (2^240 apart in
+    softmax weight): running-max rescaling (16-row kernel) and the exponent-
+    origin redo (128-row kernel) must both reach the oracle's result."""
+    x = gen.make_decode([300, 150, 2000], s_q=1, h_q=h_q, causal=False, seed=50)
+    one, two = gen.f32_to_bf16_bits(np.float32(1.0)), gen.f32_to_bf16_bits(np.float32(2.0))
+    x.q[:] = one
+    for b, hot in enumerate([100, 149, 1500]):
+        first = x.block_table[b, 0]
+        x.kv[first, 0, :] = gen.f32_to_bf16_bits(np.float32(-2.0))   # score -1152 * scale
+        page, slot = x.block_table[b, hot // 64], hot % 64
+        x.kv[page, slot, :] = two                                     # score +1152 * scale
+    _check(x, what="score growth h_q=%d" % h_q)
