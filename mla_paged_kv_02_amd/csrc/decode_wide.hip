@@ -12,26 +12,45 @@
 //    512 value dims (O^T: 16 blocks of 32x32 fp32 = 256 accumulator
 //    registers) and keeps its Q^T fragments in registers (36 k-steps of 16
 //    dims), so no cross-wave merge is ever needed.
-//  * The cache streams through LDS in 32-token tiles (36,864 B), filled by
-//    direct global->LDS DMA (buffer_load ... lds, 16 B per lane) three tiles
-//    ahead; tokens outside the part arrive as zeros through the buffer
-//    descriptor's range check.  A tile never crosses a page (tiles are
-//    32-token aligned).  The 16-byte chunk index is XOR-swizzled per row so
-//    both read patterns below are free of bank conflicts.
+//  * The cache streams through LDS in 32-token tiles (36,864 B) held in four
+//    stages: while tile t is multiplied by Q, tile t - 1 is still read for
+//    the value product and tiles t + 1, t + 2 are in flight.  Tiles arrive by
+//    direct global->LDS DMA (buffer_load ... lds, 16 B per lane); tokens
+//    outside the part read as zeros through the buffer descriptor's range
+//    check.  A tile never crosses a page (tiles are 32-token aligned).  In
+//    LDS a tile is 36 blocks of 8 rows x 8 chunks of 16 B (one DMA
+//    instruction each, block (row group i, chunk group j) at (4 j + i) KB);
+//    wave w fetches row group w, so a lane's global offset is the same in
+//    all nine of its instructions and only scalar offsets move.  Inside a
+//    block the chunk index is XOR-swizzled by row so both read patterns
+//    below are free of bank conflicts.  Page numbers come from a 64-entry
+//    window of the block table held one per lane.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K from LDS with
 //    ds_read_b128, B = Q^T from registers).  Its accumulator layout holds 16
 //    keys of one query row per lane, which is directly the P^T operand of the
 //    value product (keys mapped consistently on both sides).
 //  * O^T += V^T P^T on the same MFMA; V^T fragments come from LDS through
 //    ds_read_b64_tr_b16 (two 4-key reads per 8-key operand).
+//  * Software pipeline, one wave per SIMD: iteration t issues the QK^T chain
+//    of tile t with the DMA of tile t + 2 threaded through it, then the
+//    softmax of tile t interleaved with the value product of tile t - 1, so
+//    the matrix pipe has independent work while the wave does vector math.
 //  * Online softmax in fp32, log2 domain, with exact and bf16-rounded sums as
 //    in decode.hip.  O is never rescaled inside the tile loop (it lives in
 //    the 256 accumulator registers, and any VALU rescale would force copies
 //    of all of them through VGPRs): a row's first visible key sets its
 //    exponent origin, and if a later score exceeds the origin by more than
 //    64 (weights stay below 2^64, far from fp32 overflow) the workgroup
-//    redoes the segment with the larger origin.  Real attention scores never
-//    grow like that after the first key, so the redo is a correctness path.
+//    redoes the segment once, with each row's maximum score over the segment
+//    as its origin, which no score can exceed: at most two passes.  Real
+//    attention scores never grow like that after the first key, so the redo
+//    is a correctness path.
+//
+// The QK^T chains and the DMA are inline assembly (below); everything they
+// touch is passed as operands, M0 -- which the LDS DMA takes its
+// destination from -- is set inside each block before use (no other code in
+// this kernel uses M0), and the blocks that add scalar offsets declare SCC
+// clobbered.
 #include "mla_device.h"
 #include "kernels.h"
 
@@ -43,54 +62,108 @@ constexpr int kWRows = 32 * kWWaves;                 // 128 query rows per workg
 static_assert(kWRows == kWideRows, "row tile of the wide kernel");
 constexpr int kTileKeys = 32;
 constexpr int kRowChunks = kDqk / 8;                 // 72 chunks of 16 B per cache row
-constexpr int kTileChunks = kTileKeys * kRowChunks;  // 2304
-constexpr int kTileBytes = kTileChunks * 16;         // 36864
-constexpr int kStages = 3;                           // tiles in LDS (two in flight)
-constexpr int kDmaPerWave = kTileChunks / 64 / kWWaves;   // 9 instructions of 1 KB
+constexpr int kTileBytes = kTileKeys * kRowChunks * 16;   // 36864
+constexpr int kStages = 4;
 constexpr int kKSteps = kDqk / 16;                   // 36
 constexpr int kDBlocks = kDv / 32;                   // 16
 constexpr float kWOriginSlack = 64.0f;   // log2 units
 constexpr int kPvAhead = 2;              // value fragments (pairs of reads) read ahead
 
 typedef char __attribute__((address_space(3))) lds_char_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// chunk swizzle: row r's 16-byte chunk c lives at slot 72 r + (c ^ swz(r))
+// chunk swizzle inside a block: tile row r's chunk c (mod 8) sits at block
+// position c ^ swz(r)
 __device__ __forceinline__ int swz(int r) { return ((2 * (r & 7)) ^ ((r >> 2) & 3)) & 7; }
-__device__ __forceinline__ int slot_of(int r, int c) { return kRowChunks * r + (c ^ swz(r)); }
-
-// This wave's share of the DMA for tile T (tokens [32T, 32T + 32)) of one
-// sequence.  LDS slot q = 64 i + lane of instruction i receives cache chunk
-// (r, c) with slot_of(r, c) = q.  Tokens outside [kbeg, kend) read as zero.
-__device__ __forceinline__ void dma_tile(lds_char_t *buf, const uint16_t *kv, int page, int T,
-                                         int kbeg, int kend, int wave, int lane)
+// LDS byte offset (within a stage) of tile row r, chunk c
+__device__ __forceinline__ int tile_off(int r, int c)
 {
-    const __amdgpu_buffer_rsrc_t rsrc =
-        make_rsrc(reinterpret_cast<const char *>(kv) + (int64_t)page * kPageBytes, kPageBytes);
-    const int row0 = (T & 1) * kTileKeys;   // tile's first row inside its page
-    // recompute the per-lane offsets each tile rather than keep 9 of them live
-    asm volatile("" : "+v"(lane));
-#pragma unroll
-    for (int u = 0; u < kDmaPerWave; ++u) {
-        const int i = wave * kDmaPerWave + u;
-        const int q = 64 * i + lane;
-        const int r = q / kRowChunks;
-        const int c = (q - kRowChunks * r) ^ swz(r);
-        const int key = T * kTileKeys + r;
-        const int voff =
-            (key >= kbeg && key < kend) ? (row0 + r) * kRowBytes + 16 * c : 0x40000000;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void __attribute__((address_space(3))) *)(buf + 1024 * i), 16, voff, 0, 0, 0);
-    }
+    return 1024 * (4 * (c >> 3) + (r >> 3)) + 128 * (r & 7) + 16 * ((c & 7) ^ swz(r));
+}
+
+// One wave's DMA of one tile: rows 8 wave .. 8 wave + 7, all 72 chunks, as
+// nine 1 KB blocks.  Lane l fetches row 8 wave + l / 8, chunk
+// 8 j + ((l % 8) ^ swz(row)) into block position l of block j.
+struct TileDma {
+    u32x4_t rsrc;   // buffer descriptor of the tile's page
+    int voff;       // lane's byte offset in the page (0x40000000 = outside: zeros)
+    int soff;       // page offset of this wave's row group
+    int m0;         // LDS address of this wave's block of chunk group 0
+};
+
+__device__ __forceinline__ TileDma tile_dma(const uint16_t *kv, int page, int T, int kbeg,
+                                            int kend, int wave, int trow, int lane_off,
+                                            int stage_addr)
+{
+    const uint64_t base = reinterpret_cast<uint64_t>(kv) + (uint64_t)page * kPageBytes;
+    TileDma a;
+    a.rsrc = u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, (uint32_t)kPageBytes,
+                     0x00020000u};
+    const int key = T * kTileKeys + trow;
+    a.voff = (key >= kbeg && key < kend) ? lane_off : 0x40000000;
+    a.soff = ((T & 1) * kTileKeys + 8 * wave) * kRowBytes;
+    a.m0 = stage_addr + 1024 * wave;
+    return a;
+}
+
+__device__ __forceinline__ void dma_issue(const TileDma &a)
+{
+    int tmp;
+    asm volatile(
+        "s_mov_b32 m0, %4\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %2, %1, %3 offen lds\n"
+        "s_add_u32 m0, %4, 4096\n"
+        "s_add_u32 %0, %3, 128\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "s_add_u32 m0, %4, 8192\n"
+        "s_add_u32 %0, %3, 256\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "s_add_u32 m0, %4, 12288\n"
+        "s_add_u32 %0, %3, 384\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "s_add_u32 m0, %4, 16384\n"
+        "s_add_u32 %0, %3, 512\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "s_add_u32 m0, %4, 20480\n"
+        "s_add_u32 %0, %3, 640\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "s_add_u32 m0, %4, 24576\n"
+        "s_add_u32 %0, %3, 768\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "s_add_u32 m0, %4, 28672\n"
+        "s_add_u32 %0, %3, 896\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "s_add_u32 m0, %4, 32768\n"
+        "s_add_u32 %0, %3, 1024\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        : "=&s"(tmp)
+        : "s"(a.rsrc), "v"(a.voff), "s"(a.soff), "s"(a.m0)
+        : "memory", "scc");
 }
 
 // S^T[32 keys][32 rows] = K Q^T over the 576 dims of one 32-token tile: 36
 // v_mfma_f32_32x32x16_bf16 with A = K rows from LDS (ds_read_b128, four in
-// flight) and B = Q^T from registers.  The chain is written out here so that
-// its accumulator lives in VGPRs while the value accumulators occupy all 256
-// AGPRs.  Hazards the compiler cannot see inside the block are covered in
-// it: each MFMA waits for its own K fragment (LDS returns in order), chained
-// MFMAs accumulate into exactly the same registers (forwarded back to back),
-// and 24 wait states after the last one cover the longest XDL-write ->
-// VALU-access requirement (12 on gfx950) before the caller reads S.
+// flight; k-step kk reads kb[kk % 4] + 4096 (kk / 4)) and B = Q^T from
+// registers.  The chain is written out here so that its accumulator lives
+// in VGPRs while the value accumulators occupy all 256 AGPRs.  Hazards the
+// compiler cannot see inside the block are covered in it: each MFMA waits
+// for its own K fragment (LDS returns in order; earlier outstanding LDS or
+// scalar loads only make the counts stricter), chained MFMAs accumulate
+// into exactly the same registers (forwarded back to back), a DMA waits one
+// state after writing M0 (its immediate offset stays 0: on an LDS DMA it
+// would move the LDS destination too), and 24 wait states after the last MFMA cover the
+// longest XDL-write -> VALU-access requirement (12 on gfx950) before the
+// caller reads S.  The DMA variant threads the next tile's nine DMA
+// instructions through the chain so their issue overlaps the matrix work.
 #define MLA_QF(i) "v"(qf[i])
 __device__ __forceinline__ void qk_tile(f32x16_t &s, const int kb[4], const bf16x8_t qf[kKSteps])
 {
@@ -102,100 +175,100 @@ __device__ __forceinline__ void qk_tile(f32x16_t &s, const int kb[4], const bf16
         "ds_read_b128 %4, %8\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %1, %9, 0\n"
-        "ds_read_b128 %1, %5 offset:128\n"
+        "ds_read_b128 %1, %5 offset:4096\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %2, %10, %0\n"
-        "ds_read_b128 %2, %6 offset:128\n"
+        "ds_read_b128 %2, %6 offset:4096\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %11, %0\n"
-        "ds_read_b128 %3, %7 offset:128\n"
+        "ds_read_b128 %3, %7 offset:4096\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %4, %12, %0\n"
-        "ds_read_b128 %4, %8 offset:128\n"
+        "ds_read_b128 %4, %8 offset:4096\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %1, %13, %0\n"
-        "ds_read_b128 %1, %5 offset:256\n"
+        "ds_read_b128 %1, %5 offset:8192\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %2, %14, %0\n"
-        "ds_read_b128 %2, %6 offset:256\n"
+        "ds_read_b128 %2, %6 offset:8192\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %15, %0\n"
-        "ds_read_b128 %3, %7 offset:256\n"
+        "ds_read_b128 %3, %7 offset:8192\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %4, %16, %0\n"
-        "ds_read_b128 %4, %8 offset:256\n"
+        "ds_read_b128 %4, %8 offset:8192\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %1, %17, %0\n"
-        "ds_read_b128 %1, %5 offset:384\n"
+        "ds_read_b128 %1, %5 offset:12288\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %2, %18, %0\n"
-        "ds_read_b128 %2, %6 offset:384\n"
+        "ds_read_b128 %2, %6 offset:12288\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %19, %0\n"
-        "ds_read_b128 %3, %7 offset:384\n"
+        "ds_read_b128 %3, %7 offset:12288\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %4, %20, %0\n"
-        "ds_read_b128 %4, %8 offset:384\n"
+        "ds_read_b128 %4, %8 offset:12288\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %1, %21, %0\n"
-        "ds_read_b128 %1, %5 offset:512\n"
+        "ds_read_b128 %1, %5 offset:16384\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %2, %22, %0\n"
-        "ds_read_b128 %2, %6 offset:512\n"
+        "ds_read_b128 %2, %6 offset:16384\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %23, %0\n"
-        "ds_read_b128 %3, %7 offset:512\n"
+        "ds_read_b128 %3, %7 offset:16384\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %4, %24, %0\n"
-        "ds_read_b128 %4, %8 offset:512\n"
+        "ds_read_b128 %4, %8 offset:16384\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %1, %25, %0\n"
-        "ds_read_b128 %1, %5 offset:640\n"
+        "ds_read_b128 %1, %5 offset:20480\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %2, %26, %0\n"
-        "ds_read_b128 %2, %6 offset:640\n"
+        "ds_read_b128 %2, %6 offset:20480\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %27, %0\n"
-        "ds_read_b128 %3, %7 offset:640\n"
+        "ds_read_b128 %3, %7 offset:20480\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %4, %28, %0\n"
-        "ds_read_b128 %4, %8 offset:640\n"
+        "ds_read_b128 %4, %8 offset:20480\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %1, %29, %0\n"
-        "ds_read_b128 %1, %5 offset:768\n"
+        "ds_read_b128 %1, %5 offset:24576\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %2, %30, %0\n"
-        "ds_read_b128 %2, %6 offset:768\n"
+        "ds_read_b128 %2, %6 offset:24576\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %31, %0\n"
-        "ds_read_b128 %3, %7 offset:768\n"
+        "ds_read_b128 %3, %7 offset:24576\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %4, %32, %0\n"
-        "ds_read_b128 %4, %8 offset:768\n"
+        "ds_read_b128 %4, %8 offset:24576\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %1, %33, %0\n"
-        "ds_read_b128 %1, %5 offset:896\n"
+        "ds_read_b128 %1, %5 offset:28672\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %2, %34, %0\n"
-        "ds_read_b128 %2, %6 offset:896\n"
+        "ds_read_b128 %2, %6 offset:28672\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %35, %0\n"
-        "ds_read_b128 %3, %7 offset:896\n"
+        "ds_read_b128 %3, %7 offset:28672\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %4, %36, %0\n"
-        "ds_read_b128 %4, %8 offset:896\n"
+        "ds_read_b128 %4, %8 offset:28672\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %1, %37, %0\n"
-        "ds_read_b128 %1, %5 offset:1024\n"
+        "ds_read_b128 %1, %5 offset:32768\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %2, %38, %0\n"
-        "ds_read_b128 %2, %6 offset:1024\n"
+        "ds_read_b128 %2, %6 offset:32768\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %39, %0\n"
-        "ds_read_b128 %3, %7 offset:1024\n"
+        "ds_read_b128 %3, %7 offset:32768\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %4, %40, %0\n"
-        "ds_read_b128 %4, %8 offset:1024\n"
+        "ds_read_b128 %4, %8 offset:32768\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %1, %41, %0\n"
         "s_waitcnt lgkmcnt(2)\n"
@@ -217,7 +290,204 @@ __device__ __forceinline__ void qk_tile(f32x16_t &s, const int kb[4], const bf16
           MLA_QF(35)
         : "memory");
 }
+
+__device__ __forceinline__ void qk_tile_dma(f32x16_t &s, const int kb[4],
+                                            const bf16x8_t qf[kKSteps], const TileDma &a)
+{
+    bf16x8_t k0, k1, k2, k3;
+    int tmp;
+    asm volatile(
+        "ds_read_b128 %1, %6\n"
+        "ds_read_b128 %2, %7\n"
+        "ds_read_b128 %3, %8\n"
+        "ds_read_b128 %4, %9\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %10, 0\n"
+        "ds_read_b128 %1, %6 offset:4096\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %11, %0\n"
+        "ds_read_b128 %2, %7 offset:4096\n"
+        "s_mov_b32 m0, %49\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %47, %46, %48 offen lds\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %3, %12, %0\n"
+        "ds_read_b128 %3, %8 offset:4096\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %13, %0\n"
+        "ds_read_b128 %4, %9 offset:4096\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %14, %0\n"
+        "ds_read_b128 %1, %6 offset:8192\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %15, %0\n"
+        "ds_read_b128 %2, %7 offset:8192\n"
+        "s_add_u32 m0, %49, 4096\n"
+        "s_add_u32 %5, %48, 128\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %3, %16, %0\n"
+        "ds_read_b128 %3, %8 offset:8192\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %17, %0\n"
+        "ds_read_b128 %4, %9 offset:8192\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %18, %0\n"
+        "ds_read_b128 %1, %6 offset:12288\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %19, %0\n"
+        "ds_read_b128 %2, %7 offset:12288\n"
+        "s_add_u32 m0, %49, 8192\n"
+        "s_add_u32 %5, %48, 256\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %3, %20, %0\n"
+        "ds_read_b128 %3, %8 offset:12288\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %21, %0\n"
+        "ds_read_b128 %4, %9 offset:12288\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %22, %0\n"
+        "ds_read_b128 %1, %6 offset:16384\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %23, %0\n"
+        "ds_read_b128 %2, %7 offset:16384\n"
+        "s_add_u32 m0, %49, 12288\n"
+        "s_add_u32 %5, %48, 384\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %3, %24, %0\n"
+        "ds_read_b128 %3, %8 offset:16384\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %25, %0\n"
+        "ds_read_b128 %4, %9 offset:16384\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %26, %0\n"
+        "ds_read_b128 %1, %6 offset:20480\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %27, %0\n"
+        "ds_read_b128 %2, %7 offset:20480\n"
+        "s_add_u32 m0, %49, 16384\n"
+        "s_add_u32 %5, %48, 512\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %3, %28, %0\n"
+        "ds_read_b128 %3, %8 offset:20480\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %29, %0\n"
+        "ds_read_b128 %4, %9 offset:20480\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %30, %0\n"
+        "ds_read_b128 %1, %6 offset:24576\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %31, %0\n"
+        "ds_read_b128 %2, %7 offset:24576\n"
+        "s_add_u32 m0, %49, 20480\n"
+        "s_add_u32 %5, %48, 640\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %3, %32, %0\n"
+        "ds_read_b128 %3, %8 offset:24576\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %33, %0\n"
+        "ds_read_b128 %4, %9 offset:24576\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %34, %0\n"
+        "ds_read_b128 %1, %6 offset:28672\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %35, %0\n"
+        "ds_read_b128 %2, %7 offset:28672\n"
+        "s_add_u32 m0, %49, 24576\n"
+        "s_add_u32 %5, %48, 768\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %3, %36, %0\n"
+        "ds_read_b128 %3, %8 offset:28672\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %37, %0\n"
+        "ds_read_b128 %4, %9 offset:28672\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %38, %0\n"
+        "ds_read_b128 %1, %6 offset:32768\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %39, %0\n"
+        "ds_read_b128 %2, %7 offset:32768\n"
+        "s_add_u32 m0, %49, 28672\n"
+        "s_add_u32 %5, %48, 896\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %3, %40, %0\n"
+        "ds_read_b128 %3, %8 offset:32768\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %41, %0\n"
+        "ds_read_b128 %4, %9 offset:32768\n"
+        "s_waitcnt lgkmcnt(3)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %1, %42, %0\n"
+        "s_waitcnt lgkmcnt(2)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %43, %0\n"
+        "s_add_u32 m0, %49, 32768\n"
+        "s_add_u32 %5, %48, 1024\n"
+        "s_nop 0\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "s_waitcnt lgkmcnt(1)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %3, %44, %0\n"
+        "s_waitcnt lgkmcnt(0)\n"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %45, %0\n"
+        "s_nop 7\n"
+        "s_nop 7\n"
+        "s_nop 7\n"
+        : "=&v"(s), "=&v"(k0), "=&v"(k1), "=&v"(k2), "=&v"(k3), "=&s"(tmp)
+        : "v"(kb[0]), "v"(kb[1]), "v"(kb[2]), "v"(kb[3]),
+          MLA_QF(0), MLA_QF(1), MLA_QF(2), MLA_QF(3), MLA_QF(4), MLA_QF(5), MLA_QF(6),
+          MLA_QF(7), MLA_QF(8), MLA_QF(9), MLA_QF(10), MLA_QF(11), MLA_QF(12), MLA_QF(13),
+          MLA_QF(14), MLA_QF(15), MLA_QF(16), MLA_QF(17), MLA_QF(18), MLA_QF(19), MLA_QF(20),
+          MLA_QF(21), MLA_QF(22), MLA_QF(23), MLA_QF(24), MLA_QF(25), MLA_QF(26), MLA_QF(27),
+          MLA_QF(28), MLA_QF(29), MLA_QF(30), MLA_QF(31), MLA_QF(32), MLA_QF(33), MLA_QF(34),
+          MLA_QF(35),
+          "s"(a.rsrc), "v"(a.voff), "s"(a.soff), "s"(a.m0)
+        : "memory", "scc");
+}
 #undef MLA_QF
+
+// O^T[512 dims][32 rows] += V^T P^T for one tile: 32 MFMAs, V^T fragments of
+// (dim block d, k-step kk) at vb[read][d % 2] + 2048 kk + 4096 (d / 2) (keys
+// 16 apart are two row groups apart with the same swizzle)
+__device__ __forceinline__ void pv_tile(f32x16_t o[kDBlocks], const int vb[2][2],
+                                        bf16x8_t pf0, bf16x8_t pf1)
+{
+    i16x4_t vlo[kPvAhead], vhi[kPvAhead];
+#pragma unroll
+    for (int j = 0; j < kPvAhead; ++j) {
+        const int d = j >> 1, kk = j & 1, off = 2048 * kk + 4096 * (d >> 1);
+        vlo[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[0][d & 1] + off));
+        vhi[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[1][d & 1] + off));
+    }
+#pragma unroll
+    for (int j = 0; j < 2 * kDBlocks; ++j) {
+        const int d = j >> 1, kk = j & 1;
+        const i16x4_t lo = vlo[j % kPvAhead], hi = vhi[j % kPvAhead];
+        const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       kk ? pf1 : pf0, o[d], 0, 0, 0);
+        const int nj = j + kPvAhead;
+        if (nj < 2 * kDBlocks) {
+            const int nd = nj >> 1, nkk = nj & 1, off = 2048 * nkk + 4096 * (nd >> 1);
+            vlo[j % kPvAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[0][nd & 1] + off));
+            vhi[j % kPvAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[1][nd & 1] + off));
+        }
+    }
+}
 
 struct WideRow {
     float m;    // exponent origin (log2 units), -inf before the first visible key
@@ -225,16 +495,28 @@ struct WideRow {
     float lr;   // the same over the bf16-rounded weights (normalizes the output)
 };
 
+// the value of x in the other half of the wave (lane ^ 32), summed or maxed
+__device__ __forceinline__ float half_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
     DecodeParams p, const int32_t *__restrict__ bt, const int32_t *__restrict__ seqlens,
     const int32_t *__restrict__ meta)
 {
     __shared__ __attribute__((aligned(1024))) char tiles[kStages * kTileBytes];
-    // redo requests, by tile parity: a flag written while tile t is processed
-    // is read only after the barrier that opens tile t + 1, and written again
-    // no earlier than tile t + 2 (after the next barrier), so every wave reads
-    // the same value
-    __shared__ int redo[2];
+    // set by any wave whose rows need the segment redone; read by all after a
+    // barrier that follows every write, cleared after a second barrier
+    __shared__ int redo;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n32 = lane & 31;        // query row of this lane inside the wave's block
@@ -248,37 +530,20 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
     if (s0 < 0) return;
     const int t0 = rec[1], s1 = rec[2], t1 = rec[3], slot0 = rec[4];
     const int32_t *split_off = meta + p.num_parts * kPartInts;
-    lds_char_t *lds = (lds_char_t *)tiles;
-    const int lds_addr = (int)(uintptr_t)lds;
-    if (threadIdx.x == 0) redo[0] = redo[1] = 0;
-
-    // K^T fragment (A operand) of k-step kk: row n32, chunk 2kk + g, i.e.
-    // slot 72 n32 + 8 (kk / 4) + ((2 (kk % 4) + g) ^ swz(n32))
-    const int ksw = swz(n32);
-    int kbase[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kbase[j] = 16 * (kRowChunks * n32 + ((2 * j + g) ^ ksw));
-
-    // V^T fragment addresses: lane 16G + 4e + c (G: g' = G >> 1, h = G & 1)
-    // points at key 16 kk + 4 g' + e (+8), dims 32d + 16h + 4c .. +3, which is
-    // chunk 4d + 2h + c/2 = 8 (d / 2) + (4 (d % 2) + 2h + c/2), half c % 2
-    int vbase[2][2][2];   // [kk][second read][d parity]
+    const int lds_addr = (int)(uintptr_t)(lds_char_t *)tiles;
+    if (threadIdx.x == 0) redo = 0;
+    // the stage the first iteration's (zero-weight) value product reads must
+    // hold finite values: clear it once
     {
-        const int trG = lane >> 4;
-        const int tg = trG >> 1, th = trG & 1;
-        const int te = (lane >> 2) & 3, tc = lane & 3;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int rd = 0; rd < 2; ++rd) {
-                const int key = 16 * kk + 4 * tg + te + 8 * rd;
-#pragma unroll
-                for (int par = 0; par < 2; ++par)
-                    vbase[kk][rd][par] =
-                        16 * (kRowChunks * key + ((4 * par + 2 * th + (tc >> 1)) ^ swz(key))) +
-                        8 * (tc & 1);
-            }
+        char *z = tiles + (kStages - 1) * kTileBytes;
+        for (int i = threadIdx.x; i < kTileBytes / 16; i += kWThreads)
+            *reinterpret_cast<u32x4_t *>(z + 16 * i) = u32x4_t{0u, 0u, 0u, 0u};
     }
+
+    // DMA: this lane's tile row and its in-page offset without tile and group terms
+    const int trow = 8 * wave + (lane >> 3);
+    const int lane_off = (lane >> 3) * kRowBytes + 16 * ((lane & 7) ^ swz(trow));
+    const int row = rt * kWRows + 32 * wave + n32;
 
     for (int seq = s0; seq <= s1; ++seq) {
         const int n = seqlens[seq];
@@ -290,22 +555,40 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
         const int32_t *bt_row = bt + (int64_t)seq * p.bt_stride;
         const int T0 = ks / kTileKeys;
         const int ntiles = (ke + kTileKeys - 1) / kTileKeys - T0;
+        // block-table window: lane i holds the page of page slot pw_base + i
+        const int pg_last = (ke - 1) / kPage;
+        int pw_base = -1, pwin = 0;
+        auto window_at = [&](int base) {
+            pw_base = base;
+            pwin = base + lane <= pg_last ? bt_row[base + lane] : 0;
+        };
+        auto page_of = [&](int T) {
+            const int i = (T >> 1) - pw_base;
+            if (i >= 64) {   // uniform: move the window (every 4096 tokens)
+                window_at(pw_base + 64);
+                return __builtin_amdgcn_readlane(pwin, i - 64);
+            }
+            return __builtin_amdgcn_readlane(pwin, i);
+        };
 
-        const int row = rt * kWRows + 32 * wave + n32;
         int limit = ke;
         if (p.causal) limit = min(ke, n - p.s_q + 1 + row / p.h_q);
+        // keys below this bound are visible to every row of the wave (lane 0
+        // holds its first row, whose causal bound is the lowest)
+        const int lim_min = __builtin_amdgcn_readfirstlane(limit);
 
         bf16x8_t qf[kKSteps];
-        float m_hint = -INFINITY;     // origin floor after a redo
+        float m_hint = -INFINITY;     // origin of the second pass (segment maximum)
         WideRow st;
         f32x16_t o[kDBlocks];
         for (int attempt = 0;; ++attempt) {
-            // start the first tiles' DMA (and, once per segment, the Q^T loads)
+            if (pw_base != ks / kPage) window_at(ks / kPage);
+            // start the first two tiles' DMA (and, once per segment, the Q^T loads)
 #pragma unroll
-            for (int sg = 0; sg < kStages - 1; ++sg)
+            for (int sg = 0; sg < 2; ++sg)
                 if (sg < ntiles)
-                    dma_tile(lds + sg * kTileBytes, p.kv, bt_row[(T0 + sg) >> 1], T0 + sg, ks,
-                             ke, wave, lane);
+                    dma_issue(tile_dma(p.kv, page_of(T0 + sg), T0 + sg, ks, ke, wave, trow,
+                                       lane_off, lds_addr + sg * kTileBytes));
             if (attempt == 0) {
                 const uint16_t *qrow = p.q + ((int64_t)seq * R + row) * kDqk + 8 * g;
 #pragma unroll
@@ -313,121 +596,127 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                     qf[kk] = *reinterpret_cast<const bf16x8_t *>(qrow + 16 * kk);
             }
             st = WideRow{m_hint, 0.f, 0.f};
-            // fragment addresses in the stage of tile 0, advanced per tile
-            int kb[4], vb[2][2][2];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) kb[j] = lds_addr + kbase[j];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                vb[j >> 2][(j >> 1) & 1][j & 1] = lds_addr + vbase[j >> 2][(j >> 1) & 1][j & 1];
 #pragma unroll
             for (int d = 0; d < kDBlocks; ++d) o[d] = f32x16_t{};
 
+            // fragment addresses: K of tile t (stage t % 4), V of tile t - 1
+            int kb[4], vb[2][2];
+            {
+                int ln = lane;
+                asm volatile("" : "+v"(ln));   // derived here, not kept across attempts
+                const int r32 = ln & 31, gg = ln >> 5;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kb[j] = lds_addr + tile_off(r32, 2 * j + gg);
+                // lane 16G + 4e + c (G: g' = G >> 1, h = G & 1) points at key
+                // 16 kk + 4 g' + e (+8), dims 32d + 16h + 4c .. +3: chunk
+                // 8 (d / 2) + (4 (d % 2) + 2h + c/2), half c % 2
+                const int trG = ln >> 4;
+                const int tg = trG >> 1, th = trG & 1;
+                const int te = (ln >> 2) & 3, tc = ln & 3;
+#pragma unroll
+                for (int rd = 0; rd < 2; ++rd) {
+                    const int key = 4 * tg + te + 8 * rd;
+#pragma unroll
+                    for (int par = 0; par < 2; ++par)
+                        vb[rd][par] = lds_addr + (kStages - 1) * kTileBytes +
+                                      tile_off(key, 4 * par + 2 * th + (tc >> 1)) + 8 * (tc & 1);
+                }
+            }
+
+            // P^T operands of the previous tile (zero before the first: that
+            // iteration's value product adds nothing)
+            bf16x8_t pp0 = {}, pp1 = {};
+            bool low_any = false;         // some row of the wave outgrew its origin
+            float mrun = -INFINITY;       // running maximum of the row's scores
             for (int t = 0; t < ntiles; ++t) {
                 const int T = T0 + t;
-                // wait for this wave's part of tile t (tile t + 1 may still be
+                // this wave's part of tile t has landed (tile t + 1 may still be
                 // in flight); the barrier makes the tile visible and guarantees
-                // every wave is done with tile t - 1, whose buffer the DMA for
-                // tile t + 2 reuses
+                // every wave is done with iteration t - 1, i.e. with tile t - 2,
+                // whose stage the DMA for tile t + 2 reuses
                 if (t + 1 < ntiles)
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");
+                    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
                 else
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
-                if (t > 0 && redo[(t - 1) & 1]) break;   // uniform: a redo was asked for
-                if (t + kStages - 1 < ntiles)
-                    dma_tile(lds + ((t + kStages - 1) % kStages) * kTileBytes, p.kv,
-                             bt_row[(T + kStages - 1) >> 1], T + kStages - 1, ks, ke, wave, lane);
-                // ---- S^T[32 keys][32 rows] = K Q^T ----
-                f32x16_t s;
-                qk_tile(s, kb, qf);
 
-                // ---- mask, exponent origin, weights (lane: row n32, keys
-                //      8(r/4) + 4g + r%4 of the tile) ----
-                float tmax = -INFINITY;
+                // ---- S^T[32 keys][32 rows] = K Q^T (+ DMA of tile t + 2) ----
+                f32x16_t s;
+                if (t + 2 < ntiles)
+                    qk_tile_dma(s, kb, qf,
+                                tile_dma(p.kv, page_of(T + 2), T + 2, ks, ke, wave, trow,
+                                         lane_off, lds_addr + ((t + 2) & 3) * kTileBytes));
+                else
+                    qk_tile(s, kb, qf);
+
+                // ---- softmax of tile t (lane: row n32, keys 8(r/4) + 4g + r%4),
+                //      interleaved with the value product of tile t - 1 ----
+                if (!(T * kTileKeys >= ks && T * kTileKeys + kTileKeys <= lim_min)) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = T * kTileKeys + 8 * (r >> 2) + 4 * g + (r & 3);
-                    s[r] = (key >= ks && key < limit) ? s[r] * p.scale_log2 : -INFINITY;
-                    tmax = fmaxf(tmax, s[r]);
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = T * kTileKeys + 8 * (r >> 2) + 4 * g + (r & 3);
+                        if (!(key >= ks && key < limit)) s[r] = -INFINITY;
+                    }
                 }
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                float tmax = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+                for (int r = 3; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+                tmax = half_max(tmax) * p.scale_log2;
                 if (st.m == -INFINITY) st.m = tmax;   // first visible key: O, l still 0
-                if (tmax > st.m + kWOriginSlack) {    // origin too low: redo the segment
-                    m_hint = tmax;
-                    redo[t & 1] = 1;
-                }
+                mrun = fmaxf(mrun, tmax);
+                // origin too low: redo (never in the second pass, whose origin
+                // is the segment maximum)
+                low_any |= __builtin_amdgcn_ballot_w64(tmax > st.m + kWOriginSlack) != 0;
                 const float m_use = st.m == -INFINITY ? 0.f : st.m;
                 uint32_t pw[8];
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
-                    const float e0 = fast_exp2(s[r] - m_use), e1 = fast_exp2(s[r + 1] - m_use);
+                    const float e0 = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -m_use));
+                    const float e1 = fast_exp2(__builtin_fmaf(s[r + 1], p.scale_log2, -m_use));
                     st.l += e0 + e1;
                     pw[r >> 1] = pack_bf16x2(e0, e1);
-                    st.lr += bf16_lo(pw[r >> 1]) + bf16_hi(pw[r >> 1]);
+                    st.lr = __builtin_amdgcn_fdot2_f32_bf16(
+                        __builtin_bit_cast(bf16x2_t, pw[r >> 1]),
+                        __builtin_bit_cast(bf16x2_t, 0x3F803F80u), st.lr, false);
                 }
-                // P^T operand of k-step kk: this lane's weights 8kk .. 8kk+7
-                const bf16x8_t pf0 =
-                    __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]});
-                const bf16x8_t pf1 =
-                    __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4], pw[5], pw[6], pw[7]});
+                pv_tile(o, vb, pp0, pp1);
+#pragma unroll
+                for (int j = 0; j < 2 * kPvAhead; ++j)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                for (int j = 0; j < 2 * kDBlocks; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (j + kPvAhead < 2 * kDBlocks)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                }
+                pp0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]});
+                pp1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4], pw[5], pw[6], pw[7]});
 
-                // ---- O^T[512 dims][32 rows] += V^T P^T ----
-                __builtin_amdgcn_sched_barrier(0);
-                // step j = 2 d + kk; fragments read kPvAhead steps ahead
-                i16x4_t vlo[kPvAhead], vhi[kPvAhead];
+                // next stages: K moves to tile t + 1, V to tile t
+                const int kstep = (t & 3) == 3 ? -3 * kTileBytes : kTileBytes;
+                const int vstep = ((t - 1) & 3) == 3 ? -3 * kTileBytes : kTileBytes;
 #pragma unroll
-                for (int j = 0; j < kPvAhead; ++j) {
-                    const int d = j >> 1, kk = j & 1, off = 128 * (d >> 1);
-                    vlo[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[kk][0][d & 1] + off));
-                    vhi[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[kk][1][d & 1] + off));
-                }
+                for (int j = 0; j < 4; ++j) kb[j] += kstep;
 #pragma unroll
-                for (int j = 0; j < 2 * kDBlocks; ++j) {
-                    const int d = j >> 1, kk = j & 1;
-                    const i16x4_t lo = vlo[j % kPvAhead], hi = vhi[j % kPvAhead];
-                    const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8_t, a), kk ? pf1 : pf0, o[d], 0, 0, 0);
-                    const int nj = j + kPvAhead;
-                    if (nj < 2 * kDBlocks) {
-                        const int nd = nj >> 1, nkk = nj & 1, off = 128 * (nd >> 1);
-                        vlo[j % kPvAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[nkk][0][nd & 1] + off));
-                        vhi[j % kPvAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[nkk][1][nd & 1] + off));
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < 2 * kPvAhead; ++j) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-#pragma unroll
-                for (int j = 0; j < 2 * kDBlocks; ++j) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                    if (j + kPvAhead < 2 * kDBlocks) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-                }
-                // next tile's stage
-                const int step = (t % kStages == kStages - 1) ? -(kStages - 1) * kTileBytes : kTileBytes;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) kb[j] += step;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) vb[j >> 2][(j >> 1) & 1][j & 1] += step;
+                for (int j = 0; j < 4; ++j) vb[j >> 1][j & 1] += vstep;
             }
+            // the last tile's value product (its softmax ran in the last iteration)
+            pv_tile(o, vb, pp0, pp1);
+            if (low_any) redo = 1;
             // drain the DMA pipeline; every wave sees the same redo flag
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            const int again = redo[0] | redo[1];
+            const int again = redo;
             __syncthreads();
-            if (!again) break;
-            if (threadIdx.x == 0) redo[0] = redo[1] = 0;
-            m_hint = fmaxf(m_hint, __shfl_xor(m_hint, 32));
-            m_hint = fmaxf(m_hint, st.m);
+            if (!again || attempt > 0) break;
+            if (threadIdx.x == 0) redo = 0;
+            m_hint = mrun;   // both halves of a row hold the same maximum
         }
 
         // ---- epilogue: this wave's 32 rows, no cross-wave merge ----
-        st.l += __shfl_xor(st.l, 32);
-        st.lr += __shfl_xor(st.lr, 32);
+        st.l = half_sum(st.l);
+        st.lr = half_sum(st.lr);
         const float inv = st.lr > 0.f ? 1.f / st.lr : 0.f;
         const float lse_v = st.l > 0.f ? (st.m + fast_log2(st.l)) * kLn2 : -INFINITY;
         if (nsplit == 1) {
