@@ -456,6 +456,20 @@ __device__ __forceinline__ void qk_tile_dma(f32x16_t &s, const int kb[4],
 }
 #undef MLA_QF
 
+// Value-product step j (of 32): dim block and k-step, ordered so consecutive
+// steps accumulate into different blocks
+__device__ __forceinline__ constexpr int pv_block(int j) { return 2 * (j >> 2) + (j & 1); }
+__device__ __forceinline__ constexpr int pv_kstep(int j) { return (j >> 1) & 1; }
+// the two 4-key transposed reads of (dim block d, k-step kk)
+__device__ __forceinline__ void pv_read(const int vb[2][2], int d, int kk, i16x4_t &lo, i16x4_t &hi)
+{
+    const int off = 2048 * kk + 4096 * (d >> 1);
+    lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[0][d & 1] + off));
+    hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[1][d & 1] + off));
+}
+
 // O^T[512 dims][32 rows] += V^T P^T for one tile: 32 MFMAs, V^T fragments of
 // (dim block d, k-step kk) at vb[read][d % 2] + 2048 kk + 4096 (d / 2) (keys
 // 16 apart are two row groups apart with the same swizzle)
@@ -658,37 +672,55 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                         if (!(key >= ks && key < limit)) s[r] = -INFINITY;
                     }
                 }
-                float tmax = fmaxf(fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-                for (int r = 3; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-                tmax = half_max(tmax) * p.scale_log2;
-                if (st.m == -INFINITY) st.m = tmax;   // first visible key: O, l still 0
-                mrun = fmaxf(mrun, tmax);
-                // origin too low: redo (never in the second pass, whose origin
-                // is the segment maximum)
-                low_any |= __builtin_amdgcn_ballot_w64(tmax > st.m + kWOriginSlack) != 0;
-                const float m_use = st.m == -INFINITY ? 0.f : st.m;
+                // The value product's 32 MFMAs go out one per step, in an order
+                // where consecutive ones accumulate into different blocks; after
+                // each, a slice of the softmax runs on the vector unit while the
+                // matrix unit works.  The schedule barriers keep that order.
+                float tmax = -INFINITY, m_use = 0.f;
+                float ex[16];
                 uint32_t pw[8];
+                i16x4_t vlo[kPvAhead], vhi[kPvAhead];
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float e0 = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -m_use));
-                    const float e1 = fast_exp2(__builtin_fmaf(s[r + 1], p.scale_log2, -m_use));
-                    st.l += e0 + e1;
-                    pw[r >> 1] = pack_bf16x2(e0, e1);
-                    st.lr = __builtin_amdgcn_fdot2_f32_bf16(
-                        __builtin_bit_cast(bf16x2_t, pw[r >> 1]),
-                        __builtin_bit_cast(bf16x2_t, 0x3F803F80u), st.lr, false);
-                }
-                pv_tile(o, vb, pp0, pp1);
-#pragma unroll
-                for (int j = 0; j < 2 * kPvAhead; ++j)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                for (int j = 0; j < kPvAhead; ++j) pv_read(vb, pv_block(j), pv_kstep(j), vlo[j], vhi[j]);
 #pragma unroll
                 for (int j = 0; j < 2 * kDBlocks; ++j) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    const int d = pv_block(j), kk = pv_kstep(j);
+                    {
+                        const i16x4_t lo = vlo[j % kPvAhead], hi = vhi[j % kPvAhead];
+                        const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8_t, a), kk ? pp1 : pp0, o[d], 0, 0, 0);
+                    }
                     if (j + kPvAhead < 2 * kDBlocks)
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                        pv_read(vb, pv_block(j + kPvAhead), pv_kstep(j + kPvAhead),
+                                vlo[j % kPvAhead], vhi[j % kPvAhead]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    // ---- softmax slice j of tile t (lane: row n32, keys
+                    //      8(r/4) + 4g + r%4) ----
+                    if (j < 3) {
+#pragma unroll
+                        for (int r = 6 * j; r < 6 * j + 6 && r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+                    } else if (j == 3) {
+                        tmax = half_max(tmax) * p.scale_log2;
+                        if (st.m == -INFINITY) st.m = tmax;   // first visible key: O, l still 0
+                        mrun = fmaxf(mrun, tmax);
+                        // origin too low: redo (never in the second pass, whose
+                        // origin is the segment maximum)
+                        low_any |= __builtin_amdgcn_ballot_w64(tmax > st.m + kWOriginSlack) != 0;
+                        m_use = st.m == -INFINITY ? 0.f : st.m;
+                    } else if (j < 20 && (j & 1) == 0) {
+                        const int r = j - 4;
+                        ex[r] = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -m_use));
+                        ex[r + 1] = fast_exp2(__builtin_fmaf(s[r + 1], p.scale_log2, -m_use));
+                    } else if (j < 20) {
+                        const int r = j - 5;
+                        st.l += ex[r] + ex[r + 1];
+                        pw[r >> 1] = pack_bf16x2(ex[r], ex[r + 1]);
+                        st.lr = __builtin_amdgcn_fdot2_f32_bf16(
+                            __builtin_bit_cast(bf16x2_t, pw[r >> 1]),
+                            __builtin_bit_cast(bf16x2_t, 0x3F803F80u), st.lr, false);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 pp0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]});
                 pp1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4], pw[5], pw[6], pw[7]});
