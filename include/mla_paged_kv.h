@@ -91,15 +91,20 @@ size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts);
 /*
  * Variable-length split scheduling (the FlashMLA release bullets name
  * serving batches of sequences of differing lengths as its target).  Reads
- * the sequence lengths on the
- * device (no host synchronization), cuts the flattened list of 16-token
- * chunks of all sequences into `num_parts` contiguous ranges whose sizes
- * differ by at most one chunk, and writes the metadata described above.
- * Compute once per decode step; it stays valid for every layer while the
- * lengths do not change.
+ * the sequence lengths on the device (no host synchronization) and cuts the
+ * sequences, in batch order, into `num_parts` contiguous ranges of near-equal
+ * cost, where a sequence costs its 16-token chunks plus a fixed lead of C
+ * chunks for starting it (C = 8 when s_q * h_q is a multiple of 128, else
+ * 16): with TC cost units in all and U = min(num_parts, TC), part p < U takes
+ * the chunks whose units fall in [floor(p*TC/U), floor((p+1)*TC/U)), chunk i
+ * of sequence b sitting at unit (units of the sequences before b) + C + i.
+ * A part whose range holds lead units only is empty.  Writes the metadata
+ * described above.  Compute once per decode step; it stays valid for every
+ * layer while the lengths do not change.
  *   seqlens  [device] int32 [batch], each >= 0
- *   metadata [device] int32 [mla_metadata_ints(batch, num_parts)] (output)
- *   1 <= batch <= 16384, 1 <= num_parts <= 65536.
+ *   metadata [device] int32 [mla_metadata_ints(batch, num_parts)] (output),
+ *            16-byte aligned (part records are written 16 bytes at a time)
+ *   1 <= batch <= 8192, 1 <= num_parts <= 65536.
  */
 int mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int num_parts,
                      int32_t *metadata, void *stream);

@@ -112,13 +112,16 @@ int mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int nu
 {
     if (seqlens == nullptr || metadata == nullptr)
         return fail(MLA_ERR_INVALID_ARG, "seqlens and metadata must be non-null");
+    if (!aligned(seqlens, 4) || !aligned(metadata, 16))
+        return fail(MLA_ERR_INVALID_ARG, "metadata must be 16-byte aligned, seqlens 4-byte");
     if (int st = check_rows(batch, s_q, h_q)) return st;
     if (batch > mla::kMetaMaxBatch)
         return fail(MLA_ERR_UNSUPPORTED, "batch must be <= %d (got %d)", mla::kMetaMaxBatch, batch);
     if (num_parts < 1 || num_parts > mla::kMaxParts)
         return fail(MLA_ERR_INVALID_ARG, "num_parts must be in [1, %d] (got %d)", mla::kMaxParts,
                     num_parts);
-    return hip_status(mla::launch_metadata(seqlens, batch, num_parts, metadata,
+    return hip_status(mla::launch_metadata(seqlens, batch, num_parts,
+                                           mla::schedule_lead(s_q * h_q), metadata,
                                            static_cast<hipStream_t>(stream)),
                       "metadata kernel launch");
 }

@@ -17,14 +17,10 @@
 //    the value product and tiles t + 1, t + 2 are in flight.  Tiles arrive by
 //    direct global->LDS DMA (buffer_load ... lds, 16 B per lane); tokens
 //    outside the part read as zeros through the buffer descriptor's range
-//    check.  A tile never crosses a page (tiles are 32-token aligned).  In
-//    LDS a tile is 36 blocks of 8 rows x 8 chunks of 16 B (one DMA
-//    instruction each, block (row group i, chunk group j) at (4 j + i) KB);
-//    wave w fetches row group w, so a lane's global offset is the same in
-//    all nine of its instructions and only scalar offsets move.  Inside a
-//    block the chunk index is XOR-swizzled by row so both read patterns
-//    below are free of bank conflicts.  Page numbers come from a 64-entry
-//    window of the block table held one per lane.
+//    check.  A tile never crosses a page (tiles are 32-token aligned).  The
+//    LDS layout of a tile (blocks of 8 rows x 8 chunks, swizzled) is the one
+//    in tile_layout.h; wave w fetches row group w.  Page numbers come from a
+//    64-entry window of the block table held one per lane.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K from LDS with
 //    ds_read_b128, B = Q^T from registers).  Its accumulator layout holds 16
 //    keys of one query row per lane, which is directly the P^T operand of the
@@ -53,6 +49,7 @@
 // clobbered.
 #include "mla_device.h"
 #include "kernels.h"
+#include "tile_layout.h"
 
 namespace mla {
 
@@ -60,26 +57,13 @@ constexpr int kWWaves = 4;
 constexpr int kWThreads = kWWaves * 64;
 constexpr int kWRows = 32 * kWWaves;                 // 128 query rows per workgroup
 static_assert(kWRows == kWideRows, "row tile of the wide kernel");
-constexpr int kTileKeys = 32;
-constexpr int kRowChunks = kDqk / 8;                 // 72 chunks of 16 B per cache row
-constexpr int kTileBytes = kTileKeys * kRowChunks * 16;   // 36864
 constexpr int kStages = 4;
 constexpr int kKSteps = kDqk / 16;                   // 36
 constexpr int kDBlocks = kDv / 32;                   // 16
 constexpr float kWOriginSlack = 64.0f;   // log2 units
 constexpr int kPvAhead = 2;              // value fragments (pairs of reads) read ahead
 
-typedef char __attribute__((address_space(3))) lds_char_t;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// chunk swizzle inside a block: tile row r's chunk c (mod 8) sits at block
-// position c ^ swz(r)
-__device__ __forceinline__ int swz(int r) { return ((2 * (r & 7)) ^ ((r >> 2) & 3)) & 7; }
-// LDS byte offset (within a stage) of tile row r, chunk c
-__device__ __forceinline__ int tile_off(int r, int c)
-{
-    return 1024 * (4 * (c >> 3) + (r >> 3)) + 128 * (r & 7) + 16 * ((c & 7) ^ swz(r));
-}
 
 // One wave's DMA of one tile: rows 8 wave .. 8 wave + 7, all 72 chunks, as
 // nine 1 KB blocks.  Lane l fetches row 8 wave + l / 8, chunk
@@ -556,7 +540,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
 
     // DMA: this lane's tile row and its in-page offset without tile and group terms
     const int trow = 8 * wave + (lane >> 3);
-    const int lane_off = (lane >> 3) * kRowBytes + 16 * ((lane & 7) ^ swz(trow));
+    const int lane_off = dma_lane_offset(wave, lane);
     const int row = rt * kWRows + 32 * wave + n32;
 
     for (int seq = s0; seq <= s1; ++seq) {

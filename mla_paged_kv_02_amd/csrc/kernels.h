@@ -46,16 +46,19 @@ struct AbsorbParams {
 };
 
 constexpr int kPartInts = 8;          // ints per scheduler-part record
-constexpr int kMetaMaxBatch = 16384;
+constexpr int kMetaMaxBatch = 8192;
 constexpr int kMaxParts = 65536;
 
-hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int32_t *meta,
-                           hipStream_t stream);
+hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int lead,
+                           int32_t *meta, hipStream_t stream);
 hipError_t launch_decode_r16(const DecodeParams &p, int num_parts, int row_tiles,
                              hipStream_t stream);
 // query rows per workgroup of the wide decode kernel (used when s_q*h_q is a
 // multiple of it)
 constexpr int kWideRows = 128;
+// schedule cost of starting a sequence, in chunks, for the kernel that
+// serves s_q * h_q rows (see metadata.hip)
+constexpr int schedule_lead(int rows) { return rows % kWideRows == 0 ? 8 : 16; }
 hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tiles,
                               hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, int batch, hipStream_t stream);

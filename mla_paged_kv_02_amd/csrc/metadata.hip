@@ -2,24 +2,30 @@
 //
 // The FlashMLA release ("DeepSeek publica FlashMLA como codigo abierto",
 // release bullets) targets serving batches whose sequences differ in length.
-// Here every sequence is a run of 16-token chunks; the concatenation of all
-// runs is cut into `num_parts` contiguous ranges whose sizes differ by at most
-// one chunk, so a long sequence is spread over many workgroups and short ones
-// share a workgroup.  With T chunks and P' = min(num_parts, T) used parts,
-// part p < P' covers chunks [floor(p*T/P'), floor((p+1)*T/P')) (never empty)
-// and the part owning chunk f is floor(((f+1)*P' - 1) / T); parts >= P' are
-// empty.  A sequence touched by k parts gets k partial-result slots (k = 1:
-// written in place by the decode kernel).
+// Here every sequence is a run of 16-token chunks, and a workgroup pays a
+// fixed extra cost (query load, state merge, output) each time it starts a
+// sequence.  So the schedule works on cost units: sequence b with ch_b > 0
+// chunks is C lead-in units followed by its ch_b chunk units.  The
+// concatenation of all sequences' units (TC in total) is cut into
+// U = min(num_parts, TC) ranges, part p < U covering units
+// [floor(p*TC/U), floor((p+1)*TC/U)); a part holds the chunks whose units
+// fall in its range (a range of lead-in units only makes an empty part), so a
+// part that starts a sequence gets C fewer chunks.  C is 16 chunks for the
+// 16-row kernel and 8 for the 128-row one (measured per-sequence overheads).
+// Chunk i of sequence b sits at unit cpre[b] + C + i, and the part owning
+// unit x is floor(((x+1)*U - 1) / TC).  A sequence touched by k parts gets k
+// partial-result slots (k = 1: written in place by the decode kernel).
 //
-// One workgroup of 1024 threads; lengths are read on the device, so a
-// serving loop needs no host synchronization.  Layout of the output is
-// documented with mla_metadata_ints() in the public header.
+// One workgroup of 256 threads; lengths are read on the device once (the
+// per-sequence data lives in LDS), so a serving loop needs no host
+// synchronization.  Layout of the output is documented with
+// mla_metadata_ints() in the public header.
 #include "mla_device.h"
 #include "kernels.h"
 
 namespace mla {
 
-constexpr int kMetaThreads = 1024;
+constexpr int kMetaThreads = 256;
 
 // Exclusive scan over the workgroup: shuffle scan inside each wave, then
 // every thread adds the totals of the waves before it (two barriers).
@@ -47,57 +53,82 @@ __device__ int block_exclusive_scan(int v, int *wave_tot, int &total)
     return before + inc - v;
 }
 
-__device__ __forceinline__ int part_of_chunk(int64_t f, int64_t parts, int64_t total)
+// floor(a * b / c) for a, b, c >= 0 (c > 0); 32-bit arithmetic when the
+// product fits (the usual case), else 64-bit
+__device__ __forceinline__ int muldiv(int a, int b, int c, bool small)
 {
-    return (int)(((f + 1) * parts - 1) / total);
+    if (small) return (int)((uint32_t)a * (uint32_t)b / (uint32_t)c);
+    return (int)((int64_t)a * b / c);
 }
 
-// largest b in [0, batch) with prefix[b] <= f (prefix nondecreasing, prefix[0] = 0)
-__device__ __forceinline__ int find_seq(const int *prefix, int batch, int f)
+__device__ __forceinline__ int part_of_chunk(int f, int parts, int total, bool small)
+{
+    return small ? (int)(((uint32_t)f * (uint32_t)parts + (uint32_t)parts - 1) / (uint32_t)total)
+                 : (int)(((int64_t)(f + 1) * parts - 1) / total);
+}
+
+// largest b in [0, batch) with a[b] <= x (a nondecreasing, a[0] = 0)
+__device__ __forceinline__ int find_last_le(const int *a, int batch, int x)
 {
     int lo = 0, hi = batch - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (prefix[mid] <= f) lo = mid;
+        if (a[mid] <= x) lo = mid;
         else hi = mid - 1;
     }
     return lo;
 }
 
 __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *seqlens, int batch,
-                                                               int num_parts, int32_t *meta)
+                                                               int num_parts, int lead,
+                                                               int32_t *meta)
 {
-    __shared__ int prefix[kMetaMaxBatch + 1];   // chunk offsets of the sequences
-    __shared__ int splits[kMetaMaxBatch + 1];   // partial-slot offsets
+    __shared__ int prefix[kMetaMaxBatch + 1];        // chunk offsets of the sequences
+    __shared__ int cprefix[kMetaMaxBatch + 1];       // cost-unit offsets
+    __shared__ int splits[kMetaMaxBatch + 1];        // partial-slot offsets
+    __shared__ unsigned char tail[kMetaMaxBatch];    // tokens in a sequence's last chunk
     __shared__ int scratch[kMetaThreads / 64];
     const int t = threadIdx.x;
     const int per = (batch + kMetaThreads - 1) / kMetaThreads;
     const int b0 = min(batch, t * per);
     const int b1 = min(batch, b0 + per);
 
-    int local = 0;
+    // chunk and cost-unit counts, scanned together (cost = chunks + lead * non-empty)
+    int local = 0, local_ne = 0;
     for (int b = b0; b < b1; ++b) {
-        const int ch = (max(seqlens[b], 0) + kChunk - 1) / kChunk;
+        const int n = max(seqlens[b], 0);
+        const int ch = (n + kChunk - 1) / kChunk;
         prefix[b] = ch;
+        tail[b] = (unsigned char)(n - kChunk * (ch - 1));   // 1..16 (unused when ch == 0)
         local += ch;
+        local_ne += ch > 0;
     }
-    int total = 0;
+    int total = 0, total_ne = 0;
     int run = block_exclusive_scan(local, scratch, total);
+    int run_ne = block_exclusive_scan(local_ne, scratch, total_ne);
     for (int b = b0; b < b1; ++b) {
         const int ch = prefix[b];
         prefix[b] = run;
+        cprefix[b] = run + lead * run_ne;
         run += ch;
+        run_ne += ch > 0;
     }
-    if (t == 0) prefix[batch] = total;
+    const int tc = total + lead * total_ne;
+    if (t == 0) {
+        prefix[batch] = total;
+        cprefix[batch] = tc;
+    }
     __syncthreads();
-    const int used = min(num_parts, total);   // every used part gets >= 1 chunk
+    const int used = min(num_parts, tc);
+    const bool small = (int64_t)(tc + 1) * used < 0x7FFFFFFF;
 
     local = 0;
     for (int b = b0; b < b1; ++b) {
         const int ch = prefix[b + 1] - prefix[b];
+        const int x = cprefix[b] + lead;   // unit of the first chunk
         const int ns = ch == 0 ? 0
-                               : part_of_chunk(prefix[b] + ch - 1, used, total) -
-                                     part_of_chunk(prefix[b], used, total) + 1;
+                               : part_of_chunk(x + ch - 1, used, tc, small) -
+                                     part_of_chunk(x, used, tc, small) + 1;
         splits[b] = ns;
         local += ns;
     }
@@ -119,26 +150,36 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *s
         int32_t *rec = meta + part * kPartInts;
         int r[kPartInts] = {-1, 0, -1, 0, 0, 0, 0, 0};
         if (part < used) {
-            const int f0 = (int)((int64_t)part * total / used);
-            const int f1 = (int)((int64_t)(part + 1) * total / used);
-            const int s0 = find_seq(prefix, batch, f0);
-            const int s1 = find_seq(prefix, batch, f1 - 1);
-            r[0] = s0;
-            r[1] = (f0 - prefix[s0]) * kChunk;
-            r[2] = s1;
-            r[3] = min((f1 - prefix[s1]) * kChunk, max(seqlens[s1], 0));
-            r[4] = splits[s0] + (part - part_of_chunk(prefix[s0], used, total));
+            const int x0 = muldiv(part, tc, used, small);
+            const int x1 = muldiv(part + 1, tc, used, small);
+            // first chunk at unit >= x0, one past the last chunk at unit < x1
+            const int ba = find_last_le(cprefix, batch, x0);
+            const int f0 = prefix[ba] + max(0, x0 - cprefix[ba] - lead);
+            const int bz = find_last_le(cprefix, batch, x1 - 1);
+            const int iz = x1 - 1 - cprefix[bz] - lead;
+            const int f1 = iz >= 0 ? prefix[bz] + iz + 1 : prefix[bz];
+            if (f0 < f1) {
+                const int s0 = find_last_le(prefix, batch, f0);
+                const int s1 = find_last_le(prefix, batch, f1 - 1);
+                r[0] = s0;
+                r[1] = (f0 - prefix[s0]) * kChunk;
+                r[2] = s1;
+                // ends at a chunk boundary, or at the length if it takes s1's last chunk
+                r[3] = f1 == prefix[s1 + 1] ? (f1 - 1 - prefix[s1]) * kChunk + tail[s1]
+                                            : (f1 - prefix[s1]) * kChunk;
+                r[4] = splits[s0] + (part - part_of_chunk(cprefix[s0] + lead, used, tc, small));
+            }
         }
-#pragma unroll
-        for (int i = 0; i < kPartInts; ++i) rec[i] = r[i];
+        *reinterpret_cast<int4 *>(rec) = make_int4(r[0], r[1], r[2], r[3]);
+        *reinterpret_cast<int4 *>(rec + 4) = make_int4(r[4], r[5], r[6], r[7]);
     }
 }
 
-hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int32_t *meta,
-                           hipStream_t stream)
+hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int lead,
+                           int32_t *meta, hipStream_t stream)
 {
     hipLaunchKernelGGL(metadata_kernel, dim3(1), dim3(kMetaThreads), 0, stream, seqlens, batch,
-                       num_parts, meta);
+                       num_parts, lead, meta);
     return hipGetLastError();
 }
 

@@ -1,53 +1,62 @@
 """Host-side checks of the split schedule written by mla_get_metadata.
 
-The schedule is documented in include/mla_paged_kv.h: the 16-token chunks of
-all sequences, concatenated in batch order, are cut into P' = min(num_parts, T)
-runs, part p < P' covering chunks [floor(p*T/P'), floor((p+1)*T/P')); later
-parts are empty.  `expected_metadata`
-re-derives that layout independently in Python; `check_valid` checks the
-properties any correct schedule must have (every token covered exactly once,
-in order; slot numbering consistent with the split offsets).
+The schedule is documented in include/mla_paged_kv.h: sequence b with ch_b
+> 0 chunks of 16 tokens is `lead` cost units followed by its ch_b chunk
+units; the concatenation (TC units) is cut into U = min(num_parts, TC) runs,
+part p < U taking the chunks whose units lie in [floor(p*TC/U),
+floor((p+1)*TC/U)); a run of lead units only, and parts >= U, are empty.
+`expected_metadata` re-derives that layout independently in Python, by
+walking the unit list one unit at a time; `check_valid` checks the properties
+any correct schedule must have (every token covered exactly once, in order;
+slot numbering consistent with the split offsets).
 """
 import numpy as np
 
 CHUNK = 16
+WIDE_ROWS = 128
 
 
-def expected_metadata(seqlens, num_parts):
+def lead_for(s_q, h_q):
+    """Cost of starting a sequence, in chunks, for the kernel serving s_q*h_q rows."""
+    return 8 if (s_q * h_q) % WIDE_ROWS == 0 else 16
+
+
+def expected_metadata(seqlens, num_parts, lead):
     n = np.maximum(np.asarray(seqlens, dtype=np.int64), 0)
     B, P = len(n), int(num_parts)
     ch = (n + CHUNK - 1) // CHUNK
-    pre = np.concatenate([[0], np.cumsum(ch)])
-    T = int(pre[-1])
-    U = min(P, T)                      # used (non-empty) parts
-    starts = [(p * T) // U for p in range(U + 1)] if U else [0]
-
-    def part_of(f):
-        # the used part whose chunk range holds chunk f
-        p = 0
-        while p + 1 < U and starts[p + 1] <= f:
-            p += 1
-        return p
-
-    nsplit = np.zeros(B, dtype=np.int64)
+    # the unit list: (sequence, chunk index or -1 for a lead unit)
+    units = []
     for b in range(B):
         if ch[b]:
-            nsplit[b] = part_of(pre[b + 1] - 1) - part_of(pre[b]) + 1
+            units += [(b, -1)] * lead + [(b, i) for i in range(int(ch[b]))]
+    TC = len(units)
+    U = min(P, TC)
+    part_of_unit = np.zeros(TC, dtype=np.int64)
+    for p in range(U):
+        part_of_unit[(p * TC) // U:((p + 1) * TC) // U] = p
+    # chunks of every part, in order
+    chunks = [[] for _ in range(P)]
+    for x, (b, i) in enumerate(units):
+        if i >= 0:
+            chunks[part_of_unit[x]].append((b, i))
+    nsplit = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        nsplit[b] = sum(1 for p in range(P) if any(c[0] == b for c in chunks[p]))
     split_off = np.concatenate([[0], np.cumsum(nsplit)])
     recs = np.zeros((P, 8), dtype=np.int64)
     for p in range(P):
-        if p >= U:
+        if not chunks[p]:
             recs[p, :4] = [-1, 0, -1, 0]
             continue
-        f0, f1 = starts[p], starts[p + 1]
-        s0 = int(np.searchsorted(pre, f0, side="right") - 1)
-        s1 = int(np.searchsorted(pre, f1 - 1, side="right") - 1)
+        (s0, i0), (s1, i1) = chunks[p][0], chunks[p][-1]
         recs[p, 0] = s0
-        recs[p, 1] = (f0 - pre[s0]) * CHUNK
+        recs[p, 1] = i0 * CHUNK
         recs[p, 2] = s1
-        recs[p, 3] = min((f1 - pre[s1]) * CHUNK, n[s1])
-        recs[p, 4] = split_off[s0] + (p - part_of(pre[s0]))
-    return np.concatenate([recs.ravel(), split_off, [T]]).astype(np.int32)
+        recs[p, 3] = min((i1 + 1) * CHUNK, n[s1])
+        first_part_of_s0 = min(q for q in range(P) if any(c[0] == s0 for c in chunks[q]))
+        recs[p, 4] = split_off[s0] + (p - first_part_of_s0)
+    return np.concatenate([recs.ravel(), split_off, [int(ch.sum())]]).astype(np.int32)
 
 
 def check_valid(meta, seqlens, num_parts):

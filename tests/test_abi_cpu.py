@@ -82,6 +82,8 @@ def test_other_validation(lib):
     assert lib.mla_get_metadata(None, 2, 1, 16, 4, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
     assert lib.mla_get_metadata(FAKE, 20000, 1, 16, 4, FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
     assert lib.mla_get_metadata(FAKE, 2, 1, 16, 0, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
+    # part records are stored 16 bytes at a time
+    assert lib.mla_get_metadata(FAKE, 2, 1, 16, 4, FAKE + 4, None) == _lib.MLA_ERR_INVALID_ARG
     assert lib.mla_combine(FAKE, FAKE, FAKE, 2, 1, 16, 256, FAKE, FAKE, None) == \
         _lib.MLA_ERR_UNSUPPORTED
     assert lib.mla_combine(None, FAKE, FAKE, 2, 1, 16, 512, FAKE, FAKE, None) == \

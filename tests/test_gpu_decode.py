@@ -35,7 +35,7 @@ def test_tiny_config():
 def test_memory_bound_config():
     x = gen.make_config("memory_bound")
     _, meta, parts = _check(x)
-    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts))
+    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
 
 
 def test_skewed_config():
@@ -69,7 +69,7 @@ def test_edge_lengths(s_q, h_q, causal):
 def test_forced_part_counts(num_parts):
     x = gen.make_decode([700, 3000, 65, 1, 4097], s_q=2, h_q=16, causal=True, seed=7)
     _, meta, parts = _check(x, num_parts=num_parts, what="parts=%d" % num_parts)
-    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts))
+    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
 
 
 def test_page_permutation_is_bitwise_invariant():
@@ -104,7 +104,7 @@ def test_metadata_reused_across_calls():
         gu.compare(gu.dev_to_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl,
                    "layer %d" % layer)
     m = meta.cpu().numpy()
-    assert np.array_equal(m, sc.expected_metadata(x.seqlens, parts))
+    assert np.array_equal(m, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
 
 
 def test_repeat_runs_are_bitwise_identical():
@@ -166,7 +166,7 @@ def test_forced_part_counts_wide_rows(num_parts):
     fall inside 32-token tiles and inside pages."""
     x = gen.make_decode([700, 3000, 65, 1, 4097, 0, 33], s_q=1, h_q=128, causal=False, seed=31)
     _, meta, parts = _check(x, num_parts=num_parts, what="wide parts=%d" % num_parts)
-    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts))
+    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
 
 
 @pytest.mark.parametrize("s_q,h_q", [(2, 64), (4, 32), (8, 16), (2, 128)])
