@@ -11,18 +11,25 @@
 // reads split i's lse, one wave reduction gives M and the sum, and each lane
 // accumulates 8 of the 512 dims with up to 8 splits' loads in flight -- one
 // memory round trip for the usual two to eight splits, no LDS, no barrier.
+//
 // A sequence cut into more parts (one very long sequence among short ones)
-// is merged row by row by all four waves together, each taking every 4th
-// split, with the partial sums meeting in LDS.
+// would leave a few workgroups with hundreds of round trips.  Inside a decode
+// call it is merged in two levels: workgroup z of a row group merges splits
+// [16 z, 16 z + 16) the same way and writes the result over split 16 z (no
+// other workgroup reads that range); then, after a release fence, it counts
+// itself done on the row group's counter, and the workgroup that completes
+// the count acquires and merges the ceil(k / 16) level-one results (the same
+// formula: a merge of merges is the merge of the union) and resets the
+// counter.  The standalone entry point, whose inputs are read-only, merges
+// such sequences with all four waves on each row instead.
 #include "mla_device.h"
 #include "kernels.h"
 
 namespace mla {
 
-constexpr int kCombineThreads = 256;
-constexpr int kCombineWaves = kCombineThreads / 64;
+constexpr int kCombineWaves = kCombineRows;
+constexpr int kCombineThreads = kCombineWaves * 64;
 constexpr int kCombineInflight = 8;
-constexpr int kFewSplits = 32;
 
 __device__ __forceinline__ float wave_max(float v)
 {
@@ -84,42 +91,131 @@ __device__ __forceinline__ void accumulate(const float *o_row, int64_t split_str
     }
 }
 
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineParams p)
+// One wave merges one row over `count` slots: slot k is at o_row +
+// k * slot_stride floats and lse_col[k * lse_stride]; count <= 64.
+__device__ __forceinline__ void merge_row_wave(const float *o_row, int64_t slot_stride,
+                                               const float *lse_col, int64_t lse_stride, int count,
+                                               int lane, float acc[8], float &lse_v)
+{
+    const float ls = lane < count ? lse_col[(int64_t)lane * lse_stride] : -INFINITY;
+    const float M = wave_max(ls);
+    lse_v = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (M == -INFINITY) return;
+    const float e = fast_exp2((ls - M) * kLog2e);   // 0 for absent or empty slots
+    const float total = wave_sum(e);
+    lse_v = M + fast_log2(total) * kLn2;
+    const float wl = e / total;                   // lane k holds slot k's weight
+    accumulate(o_row, slot_stride, 0, 1, count, lane,
+               [&](int k) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k)); },
+               acc);
+}
+
+// Index of the sequence whose extra workgroups include number e (extra_off
+// is an exclusive prefix, nondecreasing): the largest b with extra_off[b] <= e.
+__device__ __forceinline__ int extra_owner(const int32_t *extra_off, int batch, int e)
+{
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (extra_off[mid] <= e) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineParams p, int batch)
 {
     __shared__ float red[kCombineWaves];
     __shared__ __attribute__((aligned(16))) float part_sum[kCombineWaves - 1][kDv];
+    __shared__ int last;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int b = blockIdx.y;
+    // workgroup y < batch: sequence y, chunk 0; later ones: extra chunks of
+    // heavy sequences
+    int b = blockIdx.y, z = 0;
+    if (b >= batch) {
+        if (p.extra_off == nullptr) return;
+        const int e = b - batch;
+        if (e >= p.extra_off[batch]) return;   // unused (the grid is an upper bound)
+        b = extra_owner(p.extra_off, batch, e);
+        z = e - p.extra_off[b] + 1;
+    }
     const int first = p.split_off[b];
     const int ns = p.split_off[b + 1] - first;
     if (p.skip_single && ns == 1) return;
     const int64_t split_stride = (int64_t)p.rows * kDv;   // floats between a row's splits
+    const int row = blockIdx.x * kCombineWaves + wave;
+    const float *o_row = p.o_part + ((int64_t)first * p.rows + row) * kDv;
+    const float *lse_col = p.lse_part + (int64_t)first * p.rows + row;
 
     if (ns <= kFewSplits) {
         // one wave per row
-        const int row = blockIdx.x * kCombineWaves + wave;
         if (row >= p.rows) return;
-        const float *lse_col = p.lse_part + (int64_t)first * p.rows + row;
-        const float ls = lane < ns ? lse_col[(int64_t)lane * p.rows] : -INFINITY;
-        const float M = wave_max(ls);
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        float lse_v = -INFINITY;
-        if (M != -INFINITY) {
-            const float e = fast_exp2((ls - M) * kLog2e);   // 0 for absent splits
-            const float total = wave_sum(e);
-            lse_v = M + fast_log2(total) * kLn2;
-            const float wl = e / total;                   // lane s holds split s's weight
-            const float *o_row = p.o_part + ((int64_t)first * p.rows + row) * kDv;
-            accumulate(o_row, split_stride, 0, 1, ns, lane,
-                       [&](int s) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s)); },
-                       acc);
-        }
+        float acc[8], lse_v;
+        merge_row_wave(o_row, split_stride, lse_col, p.rows, ns, lane, acc, lse_v);
         store_row(p, b, row, lane, acc, lse_v);
         return;
     }
 
-    // many splits: the four waves merge each of the block's rows together
+    if (p.counters != nullptr) {
+        // two levels; level one: splits [16 z, 16 z + 16) -> over split 16 z
+        const int nz = (ns + kHeavyChunk - 1) / kHeavyChunk;
+        const int s0 = kHeavyChunk * z;
+        if (row < p.rows) {
+            float acc[8], lse_v;
+            merge_row_wave(o_row + s0 * split_stride, split_stride, lse_col + (int64_t)s0 * p.rows,
+                           p.rows, min(kHeavyChunk, ns - s0), lane, acc, lse_v);
+            float *dst = p.o_part + ((int64_t)(first + s0) * p.rows + row) * kDv + 8 * lane;
+            *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+            *reinterpret_cast<f32x4_t *>(dst + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+            if (lane == 0) p.lse_part[(int64_t)(first + s0) * p.rows + row] = lse_v;
+        }
+        __syncthreads();   // every wave's results issued
+        int32_t *counter = p.counters + (int64_t)p.heavy_rank[b] * kRowGroupsMax + blockIdx.x;
+        if (threadIdx.x == 0) {
+            __threadfence();   // release this workgroup's level-one results
+            last = atomicAdd(counter, 1) == nz - 1;
+        }
+        __syncthreads();
+        if (!last) return;
+        __threadfence();   // acquire the other workgroups' results
+        if (row < p.rows) {
+            // level two: the nz results sit at splits 0, 16, 32, ...
+            float acc[8], lse_v;
+            if (nz <= 64) {
+                merge_row_wave(o_row, kHeavyChunk * split_stride, lse_col,
+                               (int64_t)kHeavyChunk * p.rows, nz, lane, acc, lse_v);
+            } else {
+                float m = -INFINITY;
+                for (int k = lane; k < nz; k += 64)
+                    m = fmaxf(m, lse_col[(int64_t)k * kHeavyChunk * p.rows]);
+                m = wave_max(m);
+                lse_v = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+                if (m != -INFINITY) {
+                    float t = 0.f;
+                    for (int k = lane; k < nz; k += 64)
+                        t += fast_exp2((lse_col[(int64_t)k * kHeavyChunk * p.rows] - m) * kLog2e);
+                    lse_v = m + fast_log2(wave_sum(t)) * kLn2;
+                    accumulate(o_row, kHeavyChunk * split_stride, 0, 1, nz, lane,
+                               [&](int k) {
+                                   return fast_exp2(
+                                       (lse_col[(int64_t)k * kHeavyChunk * p.rows] - lse_v) * kLog2e);
+                               },
+                               acc);
+                }
+            }
+            store_row(p, b, row, lane, acc, lse_v);
+        }
+        if (threadIdx.x == 0) *counter = 0;   // ready for the next call
+        return;
+    }
+
+    // many splits, one level: the four waves merge each of the block's rows
+    // together
     for (int r = 0; r < kCombineWaves; ++r) {
         const int row = blockIdx.x * kCombineWaves + r;
         if (row >= p.rows) break;   // uniform
@@ -174,10 +270,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineParams 
     }
 }
 
-hipError_t launch_combine(const CombineParams &p, int batch, hipStream_t stream)
+hipError_t launch_combine(const CombineParams &p, int batch, int extra_wgs, hipStream_t stream)
 {
-    hipLaunchKernelGGL(combine_kernel, dim3((p.rows + kCombineWaves - 1) / kCombineWaves, batch),
-                       dim3(kCombineThreads), 0, stream, p);
+    hipLaunchKernelGGL(combine_kernel,
+                       dim3((p.rows + kCombineWaves - 1) / kCombineWaves, batch + extra_wgs),
+                       dim3(kCombineThreads), 0, stream, p, batch);
     return hipGetLastError();
 }
 

@@ -26,14 +26,19 @@ struct DecodeParams {
 };
 
 struct CombineParams {
-    const float *o_part;
-    const float *lse_part;
+    float *o_part;              // the two-level merge rewrites some partials in place
+    float *lse_part;
     const int32_t *split_off;   // [batch + 1]
+    // two-level merge of heavily split sequences (null: one level)
+    const int32_t *extra_off;   // [batch + 1] extra workgroups before each sequence
+    const int32_t *heavy_rank;  // [batch] heavy sequences before each sequence
+    int32_t *counters;          // [heavy rank * kRowGroupsMax + row group], zero between calls
     int rows;                   // s_q * h_q
     int skip_single;            // rows of single-split sequences are already final
     uint16_t *out;
     float *lse;
 };
+
 
 struct AbsorbParams {
     const uint16_t *x;
@@ -45,9 +50,35 @@ struct AbsorbParams {
     int batch;
 };
 
+// Sequences split more than kFewSplits ways are "heavy": with the two-level
+// merge, kHeavyChunk consecutive splits are merged per workgroup first.
+constexpr int kFewSplits = 32;
+constexpr int kHeavyChunk = 16;
+constexpr int kCombineRows = 4;                 // rows per combine workgroup
+constexpr int kRowGroupsMax = 2048 / kCombineRows;   // s_q * h_q <= 16 * 128
+
 constexpr int kPartInts = 8;          // ints per scheduler-part record
 constexpr int kMetaMaxBatch = 8192;
 constexpr int kMaxParts = 65536;
+
+// Offsets (in int32) of the metadata sections for batch B and P parts:
+// part records, split offsets [B + 1], total chunks, extra combine
+// workgroups before each sequence [B + 1], heavy rank of each sequence [B],
+// and the merge counters (zero whenever no decode call is running).
+struct MetaLayout {
+    int64_t B, P;
+    __host__ __device__ int64_t split_off() const { return kPartInts * P; }
+    __host__ __device__ int64_t total_chunks() const { return split_off() + B + 1; }
+    __host__ __device__ int64_t extra_off() const { return total_chunks() + 1; }
+    __host__ __device__ int64_t heavy_rank() const { return extra_off() + B + 1; }
+    __host__ __device__ int64_t counters() const { return heavy_rank() + B; }
+    // a heavy sequence has more than kFewSplits of the < B + P splits
+    __host__ __device__ int64_t heavy_max() const { return (B + P) / (kFewSplits + 1) + 1; }
+    __host__ __device__ int64_t ints() const { return counters() + kRowGroupsMax * heavy_max(); }
+    // extra combine workgroups per row group: sum over heavy b of
+    // ceil(ns_b / kHeavyChunk) - 1 <= (B + P) / kHeavyChunk
+    __host__ __device__ int64_t extra_max() const { return (B + P) / kHeavyChunk + 1; }
+};
 
 hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int lead,
                            int32_t *meta, hipStream_t stream);
@@ -61,7 +92,8 @@ constexpr int kWideRows = 128;
 constexpr int schedule_lead(int rows) { return rows % kWideRows == 0 ? 8 : 16; }
 hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tiles,
                               hipStream_t stream);
-hipError_t launch_combine(const CombineParams &p, int batch, hipStream_t stream);
+// `extra_wgs`: upper bound on the extra workgroups of the two-level merge
+hipError_t launch_combine(const CombineParams &p, int batch, int extra_wgs, hipStream_t stream);
 hipError_t launch_absorb(const AbsorbParams &p, int heads, hipStream_t stream);
 
 }  // namespace mla

@@ -14,6 +14,9 @@ import numpy as np
 
 CHUNK = 16
 WIDE_ROWS = 128
+FEW_SPLITS = 32        # more splits than this: two-level merge
+HEAVY_CHUNK = 16       # splits per first-level merge workgroup
+ROW_GROUPS_MAX = 512   # merge counters per heavy sequence
 
 
 def lead_for(s_q, h_q):
@@ -56,7 +59,15 @@ def expected_metadata(seqlens, num_parts, lead):
         recs[p, 3] = min((i1 + 1) * CHUNK, n[s1])
         first_part_of_s0 = min(q for q in range(P) if any(c[0] == s0 for c in chunks[q]))
         recs[p, 4] = split_off[s0] + (p - first_part_of_s0)
-    return np.concatenate([recs.ravel(), split_off, [int(ch.sum())]]).astype(np.int32)
+    # merge sections: extra workgroups of heavy (> 32-way split) sequences,
+    # their ranks, zeroed counters
+    heavy = nsplit > FEW_SPLITS
+    extra = np.where(heavy, (nsplit + HEAVY_CHUNK - 1) // HEAVY_CHUNK - 1, 0)
+    extra_off = np.concatenate([[0], np.cumsum(extra)])
+    heavy_rank = np.concatenate([[0], np.cumsum(heavy)])[:B]
+    counters = np.zeros(ROW_GROUPS_MAX * ((B + P) // (FEW_SPLITS + 1) + 1), dtype=np.int64)
+    return np.concatenate([recs.ravel(), split_off, [int(ch.sum())], extra_off, heavy_rank,
+                           counters]).astype(np.int32)
 
 
 def check_valid(meta, seqlens, num_parts):

@@ -190,3 +190,13 @@ def test_scores_growing_after_first_key(h_q):
         page, slot = x.block_table[b, hot // 64], hot % 64
         x.kv[page, slot, :] = two                                     # score +1152 * scale
     _check(x, what="score growth h_q=%d" % h_q)
+
+
+def test_two_level_merge_with_many_first_level_groups():
+    """A sequence cut into ~4000 parts: more than 64 first-level merge groups,
+    so the second level loops over them."""
+    x = gen.make_decode([70000, 100, 3], s_q=1, h_q=16, causal=False, seed=60)
+    _, meta, parts = _check(x, num_parts=4096, what="4096 parts")
+    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
+    ns = meta[8 * parts + 1] - meta[8 * parts]
+    assert ns > 64 * 16
