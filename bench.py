@@ -31,6 +31,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 D_QK, D_V = 576, 512
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+
 WORKLOADS = {
     "memory_bound": "batch 64, s_q 1, h_q 16, d 576/512, seqlens ~N(4096,1024) clipped [1,8192], "
                     "page 64, shuffled pages, bf16 N(0,1), scale 192^-0.5",
@@ -78,6 +80,40 @@ def cpu_baseline(x, min_seconds: float):
                       % (x.name, x.batch, len(times), med)}
 
 
+def source_digest():
+    """sha256 over the library's kernel and ABI sources (names and bytes)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(HERE, "mla_paged_kv_02_amd", "csrc", "*"))):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config, x):
+    """HBM bytes (fetched + written) of one mla_decode call (decode kernel +
+    combine), from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
+    profiles/hbm_traffic.json, scaled by the copy-kernel calibration there.
+    None when no record exists for this workload or the sources have changed
+    since it was taken."""
+    path = os.path.join(HERE, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest() or config not in rec.get("per_launch", {}):
+        return None
+    k = rec["per_launch"][config]
+    decode = "decode_wide_kernel" if (x.s_q * x.h_q) % 128 == 0 else "decode_r16_kernel"
+    if decode not in k or "combine_kernel" not in k:
+        return None
+    return int(sum(k[n]["fetch_bytes"] + k[n]["write_bytes"] for n in (decode, "combine_kernel")))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +127,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (no host launch cost)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, five times (the known "
+                         "byte count that scales the HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -100,6 +139,16 @@ def main():
     import torch
     import mla_paged_kv_02_amd as mla
     from mla_paged_kv_02_amd import inputs as gen
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
@@ -190,7 +239,10 @@ def main():
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roofline.update({"traffic": None, "kernel": kernel, "ms": round(decode_ms, 5)})
+    traffic = measured_traffic(args.config, x)
+    roofline.update({"traffic": traffic, "kernel": kernel, "ms": round(decode_ms, 5)})
+    if traffic is not None:
+        roofline["traffic_vs_algorithmic"] = round(traffic / nbytes, 4)
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
