@@ -31,30 +31,44 @@ namespace mla {
 
 constexpr int kMetaThreads = 256;
 
-// Exclusive scan over the workgroup: shuffle scan inside each wave, then
-// every thread adds the totals of the waves before it (two barriers).
-__device__ int block_exclusive_scan(int v, int *wave_tot, int &total)
+// Exclusive scans of two values at once over the workgroup: shuffle scans
+// inside each wave, then every thread adds the totals of the waves before it
+// (one barrier; the caller's next scan waits on its own barrier before it
+// rewrites wave_tot, so each call alternates between two halves).
+__device__ void block_exclusive_scan2(int v0, int v1, int *wave_tot, int &run0, int &run1,
+                                      int &total0, int &total1)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    int inc = v;
+    int a = v0, b = v1;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int up = __shfl_up(inc, off);
-        if (lane >= off) inc += up;
+        const int ua = __shfl_up(a, off), ub = __shfl_up(b, off);
+        if (lane >= off) {
+            a += ua;
+            b += ub;
+        }
     }
-    if (lane == 63) wave_tot[wave] = inc;
+    constexpr int kW = kMetaThreads / 64;
+    if (lane == 63) {
+        wave_tot[wave] = a;
+        wave_tot[kW + wave] = b;
+    }
     __syncthreads();
-    int before = 0;
-    total = 0;
+    int before0 = 0, before1 = 0;
+    total0 = total1 = 0;
 #pragma unroll
-    for (int w = 0; w < kMetaThreads / 64; ++w) {
-        const int tw = wave_tot[w];
-        if (w < wave) before += tw;
-        total += tw;
+    for (int w = 0; w < kW; ++w) {
+        const int t0 = wave_tot[w], t1 = wave_tot[kW + w];
+        if (w < wave) {
+            before0 += t0;
+            before1 += t1;
+        }
+        total0 += t0;
+        total1 += t1;
     }
-    __syncthreads();   // wave_tot may be rewritten by the next scan
-    return before + inc - v;
+    run0 = before0 + a - v0;
+    run1 = before1 + b - v1;
 }
 
 // floor(a * b / c) for a, b, c >= 0 (c > 0); 32-bit arithmetic when the
@@ -91,7 +105,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *s
     __shared__ int cprefix[kMetaMaxBatch + 1];       // cost-unit offsets
     __shared__ int splits[kMetaMaxBatch + 1];        // partial-slot offsets
     __shared__ unsigned char tail[kMetaMaxBatch];    // tokens in a sequence's last chunk
-    __shared__ int scratch[kMetaThreads / 64];
+    __shared__ int scratch[3][2 * kMetaThreads / 64];   // one per scan: no reuse race
     const int t = threadIdx.x;
     const int per = (batch + kMetaThreads - 1) / kMetaThreads;
     const int b0 = min(batch, t * per);
@@ -107,9 +121,8 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *s
         local += ch;
         local_ne += ch > 0;
     }
-    int total = 0, total_ne = 0;
-    int run = block_exclusive_scan(local, scratch, total);
-    int run_ne = block_exclusive_scan(local_ne, scratch, total_ne);
+    int total = 0, total_ne = 0, run = 0, run_ne = 0;
+    block_exclusive_scan2(local, local_ne, scratch[0], run, run_ne, total, total_ne);
     for (int b = b0; b < b1; ++b) {
         const int ch = prefix[b];
         prefix[b] = run;
@@ -136,8 +149,8 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *s
         splits[b] = ns;
         local += ns;
     }
-    int total_splits = 0;
-    run = block_exclusive_scan(local, scratch, total_splits);
+    int total_splits = 0, unused_run = 0, unused_total = 0;
+    block_exclusive_scan2(local, 0, scratch[1], run, unused_run, total_splits, unused_total);
     for (int b = b0; b < b1; ++b) {
         const int ns = splits[b];
         splits[b] = run;
@@ -160,9 +173,8 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *s
             local_h += 1;
         }
     }
-    int total_x = 0, total_h = 0;   // extra workgroups, heavy sequences
-    int run_x = block_exclusive_scan(local_x, scratch, total_x);
-    int run_h = block_exclusive_scan(local_h, scratch, total_h);
+    int total_x = 0, total_h = 0, run_x = 0, run_h = 0;   // extra workgroups, heavy sequences
+    block_exclusive_scan2(local_x, local_h, scratch[2], run_x, run_h, total_x, total_h);
     int32_t *extra_off = meta + L.extra_off();
     int32_t *heavy_rank = meta + L.heavy_rank();
     for (int b = b0; b < b1; ++b) {
@@ -198,8 +210,10 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *s
             const int iz = x1 - 1 - cprefix[bz] - lead;
             const int f1 = iz >= 0 ? prefix[bz] + iz + 1 : prefix[bz];
             if (f0 < f1) {
-                const int s0 = find_last_le(prefix, batch, f0);
-                const int s1 = find_last_le(prefix, batch, f1 - 1);
+                // f0 lies in sequence ba; f1 - 1 in bz unless the range ends in
+                // bz's lead units (then in the last non-empty sequence before)
+                const int s0 = ba;
+                const int s1 = iz >= 0 ? bz : find_last_le(prefix, batch, f1 - 1);
                 r[0] = s0;
                 r[1] = (f0 - prefix[s0]) * kChunk;
                 r[2] = s1;
