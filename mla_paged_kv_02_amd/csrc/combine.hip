@@ -97,6 +97,42 @@ __device__ __forceinline__ void merge_row_wave(const float *o_row, int64_t slot_
                                                const float *lse_col, int64_t lse_stride, int count,
                                                int lane, float acc[8], float &lse_v)
 {
+    if (count <= kCombineInflight) {
+        // few slots: their rows are requested together with the lse values
+        // (one memory round trip); a row of an empty slot gets weight 0
+        f32x4_t a[kCombineInflight], c[kCombineInflight];
+#pragma unroll
+        for (int u = 0; u < kCombineInflight; ++u) {
+            a[u] = c[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (u < count) {   // uniform
+                const float *src = o_row + u * slot_stride + 8 * lane;
+                a[u] = *reinterpret_cast<const f32x4_t *>(src);
+                c[u] = *reinterpret_cast<const f32x4_t *>(src + 4);
+            }
+        }
+        const float ls = lane < count ? lse_col[(int64_t)lane * lse_stride] : -INFINITY;
+        const float M = wave_max(ls);
+        lse_v = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        if (M == -INFINITY) return;
+        const float e = fast_exp2((ls - M) * kLog2e);
+        const float total = wave_sum(e);
+        lse_v = M + fast_log2(total) * kLn2;
+        const float wl = e / total;
+#pragma unroll
+        for (int u = 0; u < kCombineInflight; ++u) {
+            if (u >= count) break;   // uniform
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+            if (w == 0.f) continue;   // an empty split's row is not used
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[q] += w * a[u][q];
+                acc[q + 4] += w * c[u][q];
+            }
+        }
+        return;
+    }
     const float ls = lane < count ? lse_col[(int64_t)lane * lse_stride] : -INFINITY;
     const float M = wave_max(ls);
     lse_v = -INFINITY;
