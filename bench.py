@@ -2,7 +2,10 @@
 
 A step is one pass of the decode hot path over one batch: the split
 schedule (mla_get_metadata) and the decode with its split-KV merge
-(mla_decode).  The default workload is the memory-bound configuration
+(mla_decode); for the full-step workload also the two absorbed-weight bmms
+around it (mla_absorb_bmm: q_nope . W_UK into the latent query, o_lat . W_UV
+after), each stage timed on its own as well.  The default workload is the
+memory-bound configuration
 (batch 64, s_q 1, h_q 16, lengths ~ N(4096, 1024) clipped to [1, 8192],
 shuffled 64-token pages of 576-wide bf16 latent rows).  Inputs are resident
 in HBM before timing; the cache is replicated so consecutive steps read
@@ -40,7 +43,21 @@ WORKLOADS = {
                      "[2,8192], page 64, shuffled pages, bf16 N(0,1), scale 192^-0.5",
     "skewed": "batch 32, s_q 1, h_q 16, one seq of 131072 + 31 of 1024, page 64, bf16 N(0,1)",
     "tiny": "batch 2, s_q 1, h_q 16, seqlens {37,130}, page 64",
+    "full_step": "batch 128, h 128, 8192 tokens each, page 64, shuffled pages; q_nope [.,128] x "
+                 "W_UK[128,128,512] bmm -> latent q (+64 rope) -> paged attention -> o_lat x "
+                 "W_UV[128,512,128] bmm; bf16 N(0,1) activations and cache, N(0,0.02) weights",
 }
+
+
+def bmm_bytes_flops(batch, heads, k, n):
+    """One absorbed-weight bmm y[b,h,:] = x[b,h,:] . W[h] (x, W, y bf16)."""
+    return (batch * heads * k + heads * k * n + batch * heads * n) * 2, 2 * batch * heads * k * n
+
+
+def pctl(v):
+    v = np.asarray(v, dtype=np.float64)
+    return {"ms": round(float(np.median(v)), 5), "p10": round(float(np.percentile(v, 10)), 5),
+            "p90": round(float(np.percentile(v, 90)), 5)}
 
 
 def algorithmic_bytes(seqlens, s_q, h_q):
@@ -61,9 +78,32 @@ def algorithmic_flops(seqlens, s_q, h_q, causal):
 
 def cpu_baseline(x, min_seconds: float):
     """The fp64 oracle on the host cores, repeated over the full batch until
-    `min_seconds` of work; returns its GB/s on the same algorithmic bytes."""
+    `min_seconds` of work; returns its GB/s on the same algorithmic bytes.
+    For the full step: the oracle's fp64 chain on the first sequences, as
+    many as fit the time."""
     from oracle import oracle as orc
     threads = orc.max_threads()
+    if x.name == "full_step":
+        e = x.extra
+        done, t_all, k = 0, 0.0, 1
+        t_end = time.perf_counter() + min_seconds
+        while done < x.batch and time.perf_counter() < t_end:
+            k = min(k, x.batch - done)
+            sel = np.arange(done, done + k)
+            t0 = time.perf_counter()
+            orc.full_step(e["q_nope"][sel], e["q_rope"][sel], e["w_uk"], e["w_uv"], x.kv,
+                          x.block_table[sel], x.seqlens[sel], scale=x.scale)
+            t_all += time.perf_counter() - t0
+            done += k
+            k *= 2
+        sl = x.seqlens[:done]
+        b1, _ = bmm_bytes_flops(done, x.h_q, 128, D_V)
+        b2, _ = bmm_bytes_flops(done, x.h_q, D_V, 128)
+        nb = b1 + algorithmic_bytes(sl, 1, x.h_q) + b2
+        return {"value": round(nb / t_all / 1e9, 3), "unit": "GB/s", "cores": threads,
+                "kind": "oracle",
+                "sample": "full_step chain (fp64) on the first %d of %d sequences, %.2f s"
+                          % (done, x.batch, t_all)}
     times = []
     t_end = time.perf_counter() + min_seconds
     while True:
@@ -118,7 +158,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="memory_bound", choices=sorted(WORKLOADS))
     ap.add_argument("--replicas", type=int, default=0,
                     help="cache copies rotated over steps (0: enough for >= 1 GiB)")
@@ -171,17 +211,32 @@ def main():
     out = torch.empty((x.batch, x.s_q, x.h_q, D_V), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((x.batch, x.s_q, x.h_q), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    full = args.config == "full_step"
+    if full:
+        q_nope = to_dev(x.extra["q_nope"])
+        w_uk = to_dev(x.extra["w_uk"])
+        w_uv = to_dev(x.extra["w_uv"])
+        y = torch.empty((x.batch, x.h_q, 128), dtype=torch.bfloat16, device=dev)
 
+    # events: [start, after metadata, after W_UK bmm, after decode, after W_UV bmm]
     def step(i, ev=None):
         if ev is not None:
             ev[0].record(stream)
         mla.get_metadata(seqlens, x.s_q, x.h_q, parts, out=meta)
         if ev is not None:
             ev[1].record(stream)
+        if full:
+            mla.absorb_bmm(q_nope, w_uk, q[:, 0, :, :D_V])
+        if ev is not None:
+            ev[2].record(stream)
         mla.decode(q, kvs[i % replicas], bt, seqlens, meta, parts, scale=x.scale,
                    causal=x.causal, workspace=ws, out=out, lse=lse)
         if ev is not None:
-            ev[2].record(stream)
+            ev[3].record(stream)
+        if full:
+            mla.absorb_bmm(out[:, 0], w_uv, y)
+        if ev is not None:
+            ev[4].record(stream)
 
     graphs = []
     if args.graph:
@@ -217,17 +272,41 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     # per-call durations with HIP events on the launch stream (eager calls)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, events[i])
     torch.cuda.synchronize()
-    decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    meta_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    st_meta = pctl([e[0].elapsed_time(e[1]) for e in events])
+    st_decode = pctl([e[2].elapsed_time(e[3]) for e in events])
+    decode_ms = st_decode["ms"]
+    meta_ms = st_meta["ms"]
 
     nbytes = algorithmic_bytes(x.seqlens, x.s_q, x.h_q)
     flops = algorithmic_flops(x.seqlens, x.s_q, x.h_q, x.causal)
-    value = nbytes / (ms_step / 1e3) / 1e9
+    stages = None
+    step_bytes, step_flops = nbytes, flops
+    if full:
+        b1, f1 = bmm_bytes_flops(x.batch, x.h_q, 128, D_V)
+        b2, f2 = bmm_bytes_flops(x.batch, x.h_q, D_V, 128)
+        st_uk = pctl([e[1].elapsed_time(e[2]) for e in events])
+        st_uv = pctl([e[3].elapsed_time(e[4]) for e in events])
+        st_all = pctl([e[0].elapsed_time(e[4]) for e in events])
+
+        def stage(st, b, f):
+            sec = st["ms"] / 1e3
+            d = dict(st)
+            if b:
+                d.update({"algorithmic_bytes": b, "GB/s": round(b / sec / 1e9, 2),
+                          "hbm_frac": round(b / sec / 1e9 / HBM_PEAK_GBS, 4),
+                          "TFLOP/s": round(f / sec / 1e12, 3),
+                          "mfma_frac": round(f / sec / 1e12 / BF16_PEAK_TFLOPS, 4)})
+            return d
+        stages = {"metadata": stage(st_meta, 0, 0), "absorb_w_uk": stage(st_uk, b1, f1),
+                  "decode": stage(st_decode, nbytes, flops), "absorb_w_uv": stage(st_uv, b2, f2),
+                  "end_to_end": stage(st_all, b1 + nbytes + b2, f1 + flops + f2)}
+        step_bytes, step_flops = b1 + nbytes + b2, f1 + flops + f2
+    value = step_bytes / (ms_step / 1e3) / 1e9
     achieved = nbytes / (decode_ms / 1e3) / 1e9
     tflops = flops / (decode_ms / 1e3) / 1e12
     # the bound is whichever peak the workload's arithmetic intensity meets first
@@ -240,7 +319,8 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     traffic = measured_traffic(args.config, x)
-    roofline.update({"traffic": traffic, "kernel": kernel, "ms": round(decode_ms, 5)})
+    roofline.update({"traffic": traffic, "kernel": kernel, "ms": round(decode_ms, 5),
+                     "ms_p10": st_decode["p10"], "ms_p90": st_decode["p90"]})
     if traffic is not None:
         roofline["traffic_vs_algorithmic"] = round(traffic / nbytes, 4)
     rec = {
@@ -261,14 +341,16 @@ def main():
                    "s_q": x.s_q, "h_q": x.h_q, "num_parts": parts, "cache_replicas": replicas,
                    "parallelism": "single GPU"},
         "roofline": roofline,
-        "tflops": round(tflops, 3),
-        "tflops_frac_of_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "tflops": round(step_flops / (ms_step / 1e3) / 1e12, 3),
+        "tflops_frac_of_bf16_peak": round(step_flops / (ms_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "metadata_ms": round(meta_ms, 5),
         "host_issue_ms_per_step": round(t_issue * 1e3 / args.steps, 5),
         "launch": "hip graph replay" if graphs else "eager",
-        "algorithmic_bytes": nbytes,
-        "algorithmic_flops": flops,
+        "algorithmic_bytes": step_bytes,
+        "algorithmic_flops": step_flops,
     }
+    if stages is not None:
+        rec["stages"] = stages
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

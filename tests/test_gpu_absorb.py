@@ -17,7 +17,7 @@ def _rel_l2(a, b):
 
 
 @pytest.mark.parametrize("B,H,K,N", [(128, 8, 128, 512), (128, 8, 512, 128), (37, 3, 64, 64),
-                                     (1, 2, 32, 192)])
+                                     (1, 2, 32, 192), (70, 5, 320, 128), (9, 2, 1024, 64)])
 def test_absorb_bmm(B, H, K, N):
     rng = np.random.default_rng(B * 7 + K)
     x = gen.normal_bf16(rng, (B, H, K))
