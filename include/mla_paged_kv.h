@@ -178,7 +178,10 @@ int mla_combine(const float *o_part, const float *lse_part, const int32_t *split
  *   w [device] bf16 [heads][K][N], contiguous
  *   y [device] bf16, element (b, h, n) at y[b*y_stride_b + h*y_stride_h + n]
  * K must be a positive multiple of 32 and N of 64; strides are in elements
- * and must keep every row 16-byte aligned (multiples of 8).
+ * and must keep every row 16-byte aligned (multiples of 8).  One workgroup
+ * per head and 64 x 64 output tile: heads rounded up to 8, times
+ * N/64 * ceil(batch/64) tiles, must stay below 2^24 (MLA_ERR_UNSUPPORTED
+ * otherwise).  No device allocation; enqueued on `stream`.
  */
 int mla_absorb_bmm(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h,
                    const uint16_t *w, int heads, int K, int N,

@@ -238,6 +238,9 @@ int mla_absorb_bmm(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h,
         return fail(MLA_ERR_UNSUPPORTED, "K must be a multiple of 32 and N of 64 (got %d, %d)", K,
                     N);
     if (heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "heads must be <= 65535");
+    if ((int64_t)((heads + 7) / 8 * 8) * (N / 64) * ((batch + 63) / 64) >= (int64_t)1 << 24)
+        return fail(MLA_ERR_UNSUPPORTED, "too many (head, tile) workgroups: %d heads, N %d, batch %d",
+                    heads, N, batch);
     if (x_stride_b % 8 || x_stride_h % 8 || y_stride_b % 8 || y_stride_h % 8 ||
         x_stride_b < 0 || x_stride_h < 0 || y_stride_b < 0 || y_stride_h < 0)
         return fail(MLA_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements");
@@ -254,6 +257,7 @@ int mla_absorb_bmm(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h,
     p.y_sb = y_stride_b;
     p.y_sh = y_stride_h;
     p.batch = batch;
+    p.heads = heads;
     return hip_status(mla::launch_absorb(p, heads, static_cast<hipStream_t>(stream)),
                       "absorb kernel launch");
 }

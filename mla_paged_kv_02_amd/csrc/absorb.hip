@@ -15,7 +15,11 @@
 // once -- G = 4 for K = 128, 16 for K = 512, 8 otherwise -- and the
 // workgroup pays one memory round trip per G slabs instead of one per slab.
 // The accumulator layout puts 4 consecutive output columns in each lane, so
-// stores are 8 bytes.
+// stores are 8 bytes.  Consecutive workgroup numbers go to the eight XCDs in
+// turn, and each XCD has its own L2: the grid is numbered so that all tiles
+// of a head share an XCD (number L -> XCD L % 8, head L % 8 + 8 ((L / 8) /
+// tiles per head)), which keeps a head's x rows and W slabs in one L2
+// instead of fetching them from HBM once per XCD.
 #include "mla_device.h"
 #include "kernels.h"
 
@@ -36,9 +40,14 @@ __global__ __launch_bounds__(kAbsThreads) void absorb_kernel(AbsorbParams p)
     const int wave = threadIdx.x >> 6;
     const int r16 = lane & 15;
     const int g = lane >> 4;
-    const int n0 = blockIdx.x * kAbsBN;
-    const int m0 = blockIdx.y * kAbsBM;
-    const int h = blockIdx.z;
+    const int ntn = p.N / kAbsBN;
+    const int tiles = ntn * ((p.batch + kAbsBM - 1) / kAbsBM);   // per head
+    const int k8 = blockIdx.x >> 3;
+    const int h = (blockIdx.x & 7) + 8 * (k8 / tiles);
+    if (h >= p.heads) return;   // padding of the head count to a multiple of 8 (uniform)
+    const int t = k8 % tiles;
+    const int n0 = (t % ntn) * kAbsBN;
+    const int m0 = (t / ntn) * kAbsBM;
 
     const uint16_t *wh = p.w + (int64_t)h * p.K * p.N;
     const int brow = m0 + wave * 16 + r16;               // batch row of this lane (B operand)
@@ -109,7 +118,8 @@ __global__ __launch_bounds__(kAbsThreads) void absorb_kernel(AbsorbParams p)
 
 hipError_t launch_absorb(const AbsorbParams &p, int heads, hipStream_t stream)
 {
-    dim3 grid(p.N / kAbsBN, (p.batch + kAbsBM - 1) / kAbsBM, heads);
+    const int tiles = (p.N / kAbsBN) * ((p.batch + kAbsBM - 1) / kAbsBM);
+    const dim3 grid((unsigned)((heads + 7) / 8 * 8) * (unsigned)tiles);
     if (p.K == 4 * kAbsKSlab)
         hipLaunchKernelGGL(absorb_kernel<4>, grid, dim3(kAbsThreads), 0, stream, p);
     else if (p.K == 16 * kAbsKSlab)

@@ -48,6 +48,7 @@ struct AbsorbParams {
     uint16_t *y;
     int64_t y_sb, y_sh;
     int batch;
+    int heads;
 };
 
 // Sequences split more than kFewSplits ways are "heavy": with the two-level

@@ -93,4 +93,7 @@ def test_other_validation(lib):
         _lib.MLA_ERR_UNSUPPORTED
     assert lib.mla_absorb_bmm(FAKE, 3, 0, FAKE, 4, 128, 64, FAKE, 0, 0, 2, None) == \
         _lib.MLA_ERR_INVALID_ARG
+    # (heads rounded up to 8) x (N / 64) x ceil(batch / 64) workgroups must stay below 2^24
+    assert lib.mla_absorb_bmm(FAKE, 0, 0, FAKE, 65535, 32, 6400, FAKE, 0, 0, 192, None) == \
+        _lib.MLA_ERR_UNSUPPORTED
     assert lib.mla_device_cus(0, None) == _lib.MLA_ERR_INVALID_ARG
