@@ -43,6 +43,14 @@ WORKLOADS = {
                      "[2,8192], page 64, shuffled pages, bf16 N(0,1), scale 192^-0.5",
     "skewed": "batch 32, s_q 1, h_q 16, one seq of 131072 + 31 of 1024, page 64, bf16 N(0,1)",
     "tiny": "batch 2, s_q 1, h_q 16, seqlens {37,130}, page 64",
+    "multi_token_4": "batch 64, s_q 4 causal (multi-token / speculative decode), h_q 16, d 576/512, "
+                     "seqlens ~N(4096,1024) clipped [4,8192], page 64, shuffled pages, bf16 N(0,1)",
+    "multi_token_8": "batch 64, s_q 8 causal, h_q 16 (128 rows per sequence), d 576/512, "
+                     "seqlens ~N(4096,1024) clipped [8,8192], page 64, shuffled pages, bf16 N(0,1)",
+    "len_1k": "batch 64, s_q 1, h_q 128, every sequence 1000 tokens, page 64, shuffled pages",
+    "len_5k": "batch 64, s_q 1, h_q 128, every sequence 5000 tokens, page 64, shuffled pages",
+    "len_10k": "batch 64, s_q 1, h_q 128, every sequence 10000 tokens, page 64, shuffled pages",
+    "len_32k": "batch 64, s_q 1, h_q 128, every sequence 32000 tokens, page 64, shuffled pages",
     "full_step": "batch 128, h 128, 8192 tokens each, page 64, shuffled pages; q_nope [.,128] x "
                  "W_UK[128,128,512] bmm -> latent q (+64 rope) -> paged attention -> o_lat x "
                  "W_UV[128,512,128] bmm; bf16 N(0,1) activations and cache, N(0,0.02) weights",

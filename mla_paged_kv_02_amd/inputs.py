@@ -17,6 +17,15 @@ description).  Every cache row is 576 bf16 values (512 latent + 64 rope).
   full_step      batch 128, h 128, length 8192 each; q_nope [.,.,128],
                  W_UK [128,128,512], W_UV [128,512,128] ~ N(0, 0.02)
 
+Wider query counts and the context-length sweep (the sequential-bmm PR
+measures serving at 1000, 5000, 10000 and 32000 input tokens; these decode
+steps at those context lengths stand in for it at the kernel level):
+
+  multi_token_4  batch 64, s_q 4 causal, h_q 16, lengths ~ N(4096, 1024) in [4, 8192]
+  multi_token_8  batch 64, s_q 8 causal, h_q 16 (128 rows), same lengths
+  len_1k, len_5k, len_10k, len_32k
+                 batch 64, s_q 1, h_q 128, every length 1000 / 5000 / 10000 / 32000
+
 Q and the cache are N(0, 1) rounded once to bf16 (round to nearest even);
 scale = fp32(192 ** -0.5).  N(mu, sigma) takes sigma as the standard
 deviation; sampled lengths are rounded half-to-even, then clipped.
@@ -38,7 +47,10 @@ PAGE = 64
 SCALE = float(np.float32(192.0 ** -0.5))
 BF16_NAN = 0x7FC0
 
-CONFIG_INDEX = {"tiny": 0, "memory_bound": 1, "compute_bound": 2, "skewed": 3, "full_step": 4}
+CONFIG_INDEX = {"tiny": 0, "memory_bound": 1, "compute_bound": 2, "skewed": 3, "full_step": 4,
+                "multi_token_4": 5, "multi_token_8": 6, "len_1k": 7, "len_5k": 8, "len_10k": 9,
+                "len_32k": 10}
+SWEEP_LENGTHS = {"len_1k": 1000, "len_5k": 5000, "len_10k": 10000, "len_32k": 32000}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -105,6 +117,11 @@ def _lengths(name: str, rng: np.random.Generator) -> np.ndarray:
         return n
     if name == "full_step":
         return np.full(128, 8192, dtype=np.int32)
+    if name in ("multi_token_4", "multi_token_8"):
+        s_q = _SHAPES[name][0]
+        return np.clip(np.rint(rng.normal(4096.0, 1024.0, 64)), s_q, 8192).astype(np.int32)
+    if name in SWEEP_LENGTHS:
+        return np.full(64, SWEEP_LENGTHS[name], dtype=np.int32)
     raise KeyError(name)
 
 
@@ -114,6 +131,12 @@ _SHAPES = {  # name -> (s_q, h_q, causal)
     "compute_bound": (2, 128, True),
     "skewed": (1, 16, False),
     "full_step": (1, 128, False),
+    "multi_token_4": (4, 16, True),
+    "multi_token_8": (8, 16, True),
+    "len_1k": (1, 128, False),
+    "len_5k": (1, 128, False),
+    "len_10k": (1, 128, False),
+    "len_32k": (1, 128, False),
 }
 
 
@@ -167,7 +190,7 @@ def make_decode(seqlens, *, s_q: int, h_q: int, causal: bool, seed: int,
 
 
 def make_config(name: str, seed: Optional[int] = None) -> DecodeInputs:
-    """One of the five named workloads; seed defaults to 1000 + its index."""
+    """One of the named workloads; seed defaults to 1000 + its index."""
     if seed is None:
         seed = 1000 + CONFIG_INDEX[name]
     ss = np.random.SeedSequence(seed).spawn(5)

@@ -54,6 +54,25 @@ def test_compute_bound_config_sampled():
     _check(x, sel=sel)
 
 
+@pytest.mark.parametrize("name", ["multi_token_4", "multi_token_8"])
+def test_multi_token_configs_sampled(name):
+    """s_q 4 and 8 causal (16-row and 128-row kernels) at the memory-bound length mix."""
+    x = gen.make_config(name)
+    sel = np.unique(np.concatenate([[int(np.argmin(x.seqlens)), int(np.argmax(x.seqlens))],
+                                    np.random.default_rng(5).choice(x.batch, 4, replace=False)]))
+    _check(x, sel=sel)
+
+
+@pytest.mark.parametrize("name,nsel", [("len_1k", 6), ("len_5k", 3), ("len_10k", 2), ("len_32k", 1)])
+def test_length_sweep_configs_sampled(name, nsel):
+    """h_q 128 at context lengths 1000 ... 32000 (every sequence split over
+    several parts at the long end); the first, last and a random sequence."""
+    x = gen.make_config(name)
+    sel = np.unique(np.concatenate([[0, x.batch - 1],
+                                    np.random.default_rng(6).choice(x.batch, nsel, replace=False)]))
+    _check(x, sel=sel)
+
+
 EDGE_LENGTHS = [1, 15, 16, 17, 63, 64, 65, 0, 2, 200, 129, 31]
 
 
@@ -166,6 +185,21 @@ def test_forced_part_counts_wide_rows(num_parts):
     fall inside 32-token tiles and inside pages."""
     x = gen.make_decode([700, 3000, 65, 1, 4097, 0, 33], s_q=1, h_q=128, causal=False, seed=31)
     _, meta, parts = _check(x, num_parts=num_parts, what="wide parts=%d" % num_parts)
+    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
+
+
+@pytest.mark.parametrize("s_q,h_q,num_parts", [(4, 16, 1), (4, 16, 7), (4, 16, 300),
+                                              (3, 32, 3), (3, 32, 64), (5, 16, 11),
+                                              (1, 32, 256), (7, 16, 5)])
+def test_forced_part_counts_several_row_tiles(s_q, h_q, num_parts):
+    """16-row tiles when s_q * h_q is above 16 but not a multiple of 128 (32,
+    64, 80, 96, 112 rows: two to seven row tiles per part) under several part
+    counts: parts that hold several sequence segments, splits inside chunks
+    and pages, causal rows."""
+    x = gen.make_decode([700, 3000, 65, 1, 4097, 0, 33], s_q=s_q, h_q=h_q, causal=s_q > 1,
+                        seed=37 + s_q)
+    _, meta, parts = _check(x, num_parts=num_parts,
+                            what="row tiles s_q=%d h_q=%d parts=%d" % (s_q, h_q, num_parts))
     assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
 
 
