@@ -88,7 +88,7 @@ int mla_default_num_parts(int num_cus, int batch, int s_q, int h_q)
     (void)batch;
     if (num_cus < 1) num_cus = 1;
     const int rows = (s_q > 0 && h_q > 0) ? s_q * h_q : 16;
-    const int row_tiles = rows % mla::kWideRows == 0 ? rows / mla::kWideRows : (rows + 15) / 16;
+    const int row_tiles = mla::decode_row_tiles(rows);
     int parts = num_cus / row_tiles;
     if (parts < 1) parts = 1;
     if (parts > mla::kMaxParts) parts = mla::kMaxParts;
@@ -180,10 +180,12 @@ int mla_decode(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
     p.lse_part = lse_part;
     p.out = out;
     p.lse = lse;
-    // 128-row tiles when the rows allow (MFMA-dense), else 16-row tiles
-    const hipError_t e = rows % mla::kWideRows == 0
-                             ? mla::launch_decode_wide(p, num_parts, rows / mla::kWideRows, st)
-                             : mla::launch_decode_r16(p, num_parts, rows / 16, st);
+    // 128-row tiles (the last one possibly partly empty) from 48 rows on,
+    // else 16-row tiles
+    const int row_tiles = mla::decode_row_tiles(rows);
+    const hipError_t e = mla::use_wide(rows)
+                             ? mla::launch_decode_wide(p, num_parts, row_tiles, st)
+                             : mla::launch_decode_r16(p, num_parts, row_tiles, st);
     if (e != hipSuccess) return hip_status(e, "decode kernel launch");
 
     // the merge may rewrite partials and counters in place (see combine.hip)

@@ -1,5 +1,5 @@
-// decode_wide.hip -- paged MLA decode for 128-row query tiles (h_q * s_q a
-// multiple of 128), where QK^T and PV are dense enough to be MFMA-bound.
+// decode_wide.hip -- paged MLA decode for 128-row query tiles (h_q * s_q of
+// 48 rows or more), where QK^T and PV are dense enough to be MFMA-bound.
 //
 // Same operation as decode.hip: softmax(scale * Q K^T) V per query row over
 // the 64-token paged latent cache (FlashMLA, "DeepSeek publica FlashMLA como
@@ -11,7 +11,11 @@
 //  * 4 waves; wave w owns query rows [32w, 32w + 32) of the tile over all
 //    512 value dims (O^T: 16 blocks of 32x32 fp32 = 256 accumulator
 //    registers) and keeps its Q^T fragments in registers (36 k-steps of 16
-//    dims), so no cross-wave merge is ever needed.
+//    dims), so no cross-wave merge is ever needed.  When h_q * s_q is not a
+//    multiple of 128 the last tile is partly empty: a wave without rows only
+//    fetches its share of each tile, rows past the end read zero queries and
+//    are not written.  The cache is still streamed once per 128 rows, which
+//    beats one pass per 16-row tile from 48 rows on.
 //  * The cache streams through LDS in 32-token tiles (36,864 B) held in four
 //    stages: while tile t is multiplied by Q, tile t - 1 is still read for
 //    the value product and tiles t + 1, t + 2 are in flight.  Tiles arrive by
@@ -542,6 +546,10 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
     const int trow = 8 * wave + (lane >> 3);
     const int lane_off = dma_lane_offset(wave, lane);
     const int row = rt * kWRows + 32 * wave + n32;
+    // a row count that is not a multiple of 128 leaves the last tile partly
+    // empty: waves without rows only fetch their share of each tile
+    const bool has_rows = rt * kWRows + 32 * wave < R;   // uniform
+    const bool row_ok = row < R;
 
     for (int seq = s0; seq <= s1; ++seq) {
         const int n = seqlens[seq];
@@ -588,10 +596,11 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                     dma_issue(tile_dma(p.kv, page_of(T0 + sg), T0 + sg, ks, ke, wave, trow,
                                        lane_off, lds_addr + sg * kTileBytes));
             if (attempt == 0) {
-                const uint16_t *qrow = p.q + ((int64_t)seq * R + row) * kDqk + 8 * g;
+                const uint16_t *qrow = p.q + ((int64_t)seq * R + (row_ok ? row : 0)) * kDqk + 8 * g;
 #pragma unroll
                 for (int kk = 0; kk < kKSteps; ++kk)
-                    qf[kk] = *reinterpret_cast<const bf16x8_t *>(qrow + 16 * kk);
+                    qf[kk] = row_ok ? *reinterpret_cast<const bf16x8_t *>(qrow + 16 * kk)
+                                    : bf16x8_t{};
             }
             st = WideRow{m_hint, 0.f, 0.f};
 #pragma unroll
@@ -638,76 +647,82 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
 
-                // ---- S^T[32 keys][32 rows] = K Q^T (+ DMA of tile t + 2) ----
-                f32x16_t s;
-                if (t + 2 < ntiles)
-                    qk_tile_dma(s, kb, qf,
-                                tile_dma(p.kv, page_of(T + 2), T + 2, ks, ke, wave, trow,
-                                         lane_off, lds_addr + ((t + 2) & 3) * kTileBytes));
-                else
-                    qk_tile(s, kb, qf);
+                if (!has_rows) {
+                    if (t + 2 < ntiles)
+                        dma_issue(tile_dma(p.kv, page_of(T + 2), T + 2, ks, ke, wave, trow,
+                                           lane_off, lds_addr + ((t + 2) & 3) * kTileBytes));
+                } else {
+                    // ---- S^T[32 keys][32 rows] = K Q^T (+ DMA of tile t + 2) ----
+                    f32x16_t s;
+                    if (t + 2 < ntiles)
+                        qk_tile_dma(s, kb, qf,
+                                    tile_dma(p.kv, page_of(T + 2), T + 2, ks, ke, wave, trow,
+                                             lane_off, lds_addr + ((t + 2) & 3) * kTileBytes));
+                    else
+                        qk_tile(s, kb, qf);
 
-                // ---- softmax of tile t (lane: row n32, keys 8(r/4) + 4g + r%4),
-                //      interleaved with the value product of tile t - 1 ----
-                if (!(T * kTileKeys >= ks && T * kTileKeys + kTileKeys <= lim_min)) {
+                    // ---- softmax of tile t (lane: row n32, keys 8(r/4) + 4g + r%4),
+                    //      interleaved with the value product of tile t - 1 ----
+                    if (!(T * kTileKeys >= ks && T * kTileKeys + kTileKeys <= lim_min)) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = T * kTileKeys + 8 * (r >> 2) + 4 * g + (r & 3);
-                        if (!(key >= ks && key < limit)) s[r] = -INFINITY;
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = T * kTileKeys + 8 * (r >> 2) + 4 * g + (r & 3);
+                            if (!(key >= ks && key < limit)) s[r] = -INFINITY;
+                        }
                     }
+                    // The value product's 32 MFMAs go out one per step, in an order
+                    // where consecutive ones accumulate into different blocks; after
+                    // each, a slice of the softmax runs on the vector unit while the
+                    // matrix unit works.  The schedule barriers keep that order.
+                    float tmax = -INFINITY, m_use = 0.f;
+                    float ex[16];
+                    uint32_t pw[8];
+                    i16x4_t vlo[kPvAhead], vhi[kPvAhead];
+#pragma unroll
+                    for (int j = 0; j < kPvAhead; ++j) pv_read(vb, pv_block(j), pv_kstep(j), vlo[j], vhi[j]);
+#pragma unroll
+                    for (int j = 0; j < 2 * kDBlocks; ++j) {
+                        const int d = pv_block(j), kk = pv_kstep(j);
+                        {
+                            const i16x4_t lo = vlo[j % kPvAhead], hi = vhi[j % kPvAhead];
+                            const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(bf16x8_t, a), kk ? pp1 : pp0, o[d], 0, 0, 0);
+                        }
+                        if (j + kPvAhead < 2 * kDBlocks)
+                            pv_read(vb, pv_block(j + kPvAhead), pv_kstep(j + kPvAhead),
+                                    vlo[j % kPvAhead], vhi[j % kPvAhead]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        // ---- softmax slice j of tile t (lane: row n32, keys
+                        //      8(r/4) + 4g + r%4) ----
+                        if (j < 3) {
+#pragma unroll
+                            for (int r = 6 * j; r < 6 * j + 6 && r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+                        } else if (j == 3) {
+                            tmax = half_max(tmax) * p.scale_log2;
+                            if (st.m == -INFINITY) st.m = tmax;   // first visible key: O, l still 0
+                            mrun = fmaxf(mrun, tmax);
+                            // origin too low: redo (never in the second pass, whose
+                            // origin is the segment maximum)
+                            low_any |= __builtin_amdgcn_ballot_w64(tmax > st.m + kWOriginSlack) != 0;
+                            m_use = st.m == -INFINITY ? 0.f : st.m;
+                        } else if (j < 20 && (j & 1) == 0) {
+                            const int r = j - 4;
+                            ex[r] = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -m_use));
+                            ex[r + 1] = fast_exp2(__builtin_fmaf(s[r + 1], p.scale_log2, -m_use));
+                        } else if (j < 20) {
+                            const int r = j - 5;
+                            st.l += ex[r] + ex[r + 1];
+                            pw[r >> 1] = pack_bf16x2(ex[r], ex[r + 1]);
+                            st.lr = __builtin_amdgcn_fdot2_f32_bf16(
+                                __builtin_bit_cast(bf16x2_t, pw[r >> 1]),
+                                __builtin_bit_cast(bf16x2_t, 0x3F803F80u), st.lr, false);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    pp0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]});
+                    pp1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4], pw[5], pw[6], pw[7]});
                 }
-                // The value product's 32 MFMAs go out one per step, in an order
-                // where consecutive ones accumulate into different blocks; after
-                // each, a slice of the softmax runs on the vector unit while the
-                // matrix unit works.  The schedule barriers keep that order.
-                float tmax = -INFINITY, m_use = 0.f;
-                float ex[16];
-                uint32_t pw[8];
-                i16x4_t vlo[kPvAhead], vhi[kPvAhead];
-#pragma unroll
-                for (int j = 0; j < kPvAhead; ++j) pv_read(vb, pv_block(j), pv_kstep(j), vlo[j], vhi[j]);
-#pragma unroll
-                for (int j = 0; j < 2 * kDBlocks; ++j) {
-                    const int d = pv_block(j), kk = pv_kstep(j);
-                    {
-                        const i16x4_t lo = vlo[j % kPvAhead], hi = vhi[j % kPvAhead];
-                        const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8_t, a), kk ? pp1 : pp0, o[d], 0, 0, 0);
-                    }
-                    if (j + kPvAhead < 2 * kDBlocks)
-                        pv_read(vb, pv_block(j + kPvAhead), pv_kstep(j + kPvAhead),
-                                vlo[j % kPvAhead], vhi[j % kPvAhead]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    // ---- softmax slice j of tile t (lane: row n32, keys
-                    //      8(r/4) + 4g + r%4) ----
-                    if (j < 3) {
-#pragma unroll
-                        for (int r = 6 * j; r < 6 * j + 6 && r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-                    } else if (j == 3) {
-                        tmax = half_max(tmax) * p.scale_log2;
-                        if (st.m == -INFINITY) st.m = tmax;   // first visible key: O, l still 0
-                        mrun = fmaxf(mrun, tmax);
-                        // origin too low: redo (never in the second pass, whose
-                        // origin is the segment maximum)
-                        low_any |= __builtin_amdgcn_ballot_w64(tmax > st.m + kWOriginSlack) != 0;
-                        m_use = st.m == -INFINITY ? 0.f : st.m;
-                    } else if (j < 20 && (j & 1) == 0) {
-                        const int r = j - 4;
-                        ex[r] = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -m_use));
-                        ex[r + 1] = fast_exp2(__builtin_fmaf(s[r + 1], p.scale_log2, -m_use));
-                    } else if (j < 20) {
-                        const int r = j - 5;
-                        st.l += ex[r] + ex[r + 1];
-                        pw[r >> 1] = pack_bf16x2(ex[r], ex[r + 1]);
-                        st.lr = __builtin_amdgcn_fdot2_f32_bf16(
-                            __builtin_bit_cast(bf16x2_t, pw[r >> 1]),
-                            __builtin_bit_cast(bf16x2_t, 0x3F803F80u), st.lr, false);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                pp0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]});
-                pp1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4], pw[5], pw[6], pw[7]});
 
                 // next stages: K moves to tile t + 1, V to tile t
                 const int kstep = (t & 3) == 3 ? -3 * kTileBytes : kTileBytes;
@@ -718,7 +733,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                 for (int j = 0; j < 4; ++j) vb[j >> 1][j & 1] += vstep;
             }
             // the last tile's value product (its softmax ran in the last iteration)
-            pv_tile(o, vb, pp0, pp1);
+            if (has_rows) pv_tile(o, vb, pp0, pp1);
             if (low_any) redo = 1;
             // drain the DMA pipeline; every wave sees the same redo flag
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -735,28 +750,30 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
         st.lr = half_sum(st.lr);
         const float inv = st.lr > 0.f ? 1.f / st.lr : 0.f;
         const float lse_v = st.l > 0.f ? (st.m + fast_log2(st.l)) * kLn2 : -INFINITY;
-        if (nsplit == 1) {
-            uint16_t *dst = p.out + ((int64_t)seq * R + row) * kDv + 4 * g;
+        if (row_ok) {   // rows of a partial last tile are not written
+            if (nsplit == 1) {
+                uint16_t *dst = p.out + ((int64_t)seq * R + row) * kDv + 4 * g;
 #pragma unroll
-            for (int d = 0; d < kDBlocks; ++d)
+                for (int d = 0; d < kDBlocks; ++d)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    u32x2_t v;
-                    v[0] = pack_bf16x2(o[d][4 * q4] * inv, o[d][4 * q4 + 1] * inv);
-                    v[1] = pack_bf16x2(o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv);
-                    *reinterpret_cast<u32x2_t *>(dst + 32 * d + 8 * q4) = v;
-                }
-            if (g == 0) p.lse[(int64_t)seq * R + row] = lse_v;
-        } else {
-            float *dst = p.o_part + ((int64_t)slot * R + row) * kDv + 4 * g;
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        u32x2_t v;
+                        v[0] = pack_bf16x2(o[d][4 * q4] * inv, o[d][4 * q4 + 1] * inv);
+                        v[1] = pack_bf16x2(o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv);
+                        *reinterpret_cast<u32x2_t *>(dst + 32 * d + 8 * q4) = v;
+                    }
+                if (g == 0) p.lse[(int64_t)seq * R + row] = lse_v;
+            } else {
+                float *dst = p.o_part + ((int64_t)slot * R + row) * kDv + 4 * g;
 #pragma unroll
-            for (int d = 0; d < kDBlocks; ++d)
+                for (int d = 0; d < kDBlocks; ++d)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    *reinterpret_cast<f32x4_t *>(dst + 32 * d + 8 * q4) =
-                        f32x4_t{o[d][4 * q4] * inv, o[d][4 * q4 + 1] * inv,
-                                o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv};
-            if (g == 0) p.lse_part[(int64_t)slot * R + row] = lse_v;
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        *reinterpret_cast<f32x4_t *>(dst + 32 * d + 8 * q4) =
+                            f32x4_t{o[d][4 * q4] * inv, o[d][4 * q4 + 1] * inv,
+                                    o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv};
+                if (g == 0) p.lse_part[(int64_t)slot * R + row] = lse_v;
+            }
         }
     }
 }

@@ -90,7 +90,16 @@ hipError_t launch_decode_r16(const DecodeParams &p, int num_parts, int row_tiles
 constexpr int kWideRows = 128;
 // schedule cost of starting a sequence, in chunks, for the kernel that
 // serves s_q * h_q rows (see metadata.hip)
-constexpr int schedule_lead(int rows) { return rows % kWideRows == 0 ? 8 : 16; }
+// The 128-row kernel serves multiples of 128 rows and, with a partly empty
+// last tile, any row count from 48 on (it streams the cache once per 128
+// rows instead of once per 16); the 16-row kernel serves 16 and 32 rows.
+constexpr int kWideMinRows = 48;
+constexpr bool use_wide(int rows) { return rows % kWideRows == 0 || rows >= kWideMinRows; }
+constexpr int decode_row_tiles(int rows)
+{
+    return use_wide(rows) ? (rows + kWideRows - 1) / kWideRows : (rows + 15) / 16;
+}
+constexpr int schedule_lead(int rows) { return use_wide(rows) ? 8 : 16; }
 hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tiles,
                               hipStream_t stream);
 // `extra_wgs`: upper bound on the extra workgroups of the two-level merge

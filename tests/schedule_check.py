@@ -19,9 +19,15 @@ HEAVY_CHUNK = 16       # splits per first-level merge workgroup
 ROW_GROUPS_MAX = 512   # merge counters per heavy sequence
 
 
+WIDE_MIN_ROWS = 48
+
+
 def lead_for(s_q, h_q):
-    """Cost of starting a sequence, in chunks, for the kernel serving s_q*h_q rows."""
-    return 8 if (s_q * h_q) % WIDE_ROWS == 0 else 16
+    """Cost of starting a sequence, in chunks, for the kernel serving s_q*h_q
+    rows: 8 for the 128-row kernel (multiples of 128, or 48 rows and more),
+    16 for the 16-row kernel."""
+    r = s_q * h_q
+    return 8 if (r % WIDE_ROWS == 0 or r >= WIDE_MIN_ROWS) else 16
 
 
 def expected_metadata(seqlens, num_parts, lead):

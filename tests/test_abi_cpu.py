@@ -48,7 +48,9 @@ def test_sizes(lib):
     assert lib.mla_default_num_parts(256, 64, 1, 16) == 256
     assert lib.mla_default_num_parts(256, 128, 2, 128) == 128   # two 128-row tiles
     assert lib.mla_default_num_parts(256, 8, 1, 128) == 256     # one 128-row tile
-    assert lib.mla_default_num_parts(256, 8, 3, 32) == 42       # six 16-row tiles
+    assert lib.mla_default_num_parts(256, 8, 3, 32) == 256      # 96 rows: one partial 128-row tile
+    assert lib.mla_default_num_parts(256, 8, 5, 32) == 128      # 160 rows: two 128-row tiles
+    assert lib.mla_default_num_parts(256, 8, 2, 16) == 128      # 32 rows: two 16-row tiles
 
 
 def _decode(lib, **kw):
