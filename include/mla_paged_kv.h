@@ -109,7 +109,8 @@ size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts);
  * A part whose range holds lead units only is empty.  Writes the metadata
  * described above.  Compute once per decode step; it stays valid for every
  * layer while the lengths do not change.
- *   seqlens  [device] int32 [batch], each >= 0
+ *   seqlens  [device] int32 [batch]; a negative length counts as 0 and one
+ *            above 2^21 tokens as 2^21 (mla_decode applies the same cap)
  *   metadata [device] int32 [mla_metadata_ints(batch, num_parts)] (output),
  *            16-byte aligned (part records are written 16 bytes at a time)
  *   1 <= batch <= 8192, 1 <= num_parts <= 65536.
@@ -127,6 +128,11 @@ int mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int nu
  * where kv_row(b, j) = kv_cache[block_table[b*bt_stride + j/64]][j%64][:].
  * A row with L <= 0 gets out = 0 and lse = -inf.  Softmax runs in fp32 on
  * bf16 MFMA products; out is rounded to bf16 (nearest even).
+ * The caller keeps n <= 64*bt_stride and the entries a sequence uses in
+ * [0, num_pages).  The kernels do not report a breach (the values live on
+ * the device) but keep every read inside the buffers: n is capped at 2^21
+ * tokens, j/64 at bt_stride - 1 (keys past the table's width reuse its last
+ * column) and an entry outside [0, num_pages) reads page num_pages - 1.
  *
  *   q           [device] bf16 [batch][s_q][h_q][576]
  *   kv_cache    [device] bf16 [num_pages][64][576]

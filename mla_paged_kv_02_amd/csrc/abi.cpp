@@ -6,6 +6,8 @@
 // device memory or keeps a pointer past the call.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -169,6 +171,7 @@ int mla_decode(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
     p.kv = kv_cache;
     p.block_table = block_table;
     p.bt_stride = bt_stride;
+    p.page_max = (uint32_t)std::min<int64_t>(num_pages - 1, INT32_MAX);
     p.seqlens = seqlens;
     p.meta = metadata;
     p.num_parts = num_parts;

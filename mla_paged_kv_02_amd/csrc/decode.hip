@@ -56,7 +56,10 @@ __device__ __forceinline__ void load_chunk(ChunkRegs &k, const DecodeParams &p,
                                            const int32_t *__restrict__ bt, int seq, int c,
                                            int key_end, int r16, int g)
 {
-    const int page = bt[(int64_t)seq * p.bt_stride + (c >> 2)];
+    // columns past the table's width repeat its last one; entries outside
+    // the cache are clamped into it (negative ones too, as unsigned)
+    const int64_t col = min((int64_t)(c >> 2), p.bt_stride - 1);
+    const uint32_t page = min((uint32_t)bt[(int64_t)seq * p.bt_stride + col], p.page_max);
     const char *base = reinterpret_cast<const char *>(p.kv) + (int64_t)page * kPageBytes;
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, kPageBytes);
     const int key = c * kChunk + r16;
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
     lds_short_t *qs = (lds_short_t *)(smem + kQOffset);
 
     for (int seq = s0; seq <= s1; ++seq) {
-        const int n = seqlens[seq];
+        const int n = min(seqlens[seq], kMaxSeqLen);
         const int ks = seq == s0 ? t0 : 0;
         const int ke = seq == s1 ? t1 : n;
         if (ks >= ke) continue;   // empty sequence inside the part (uniform)

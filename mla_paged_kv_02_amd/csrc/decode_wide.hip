@@ -552,7 +552,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
     const bool row_ok = row < R;
 
     for (int seq = s0; seq <= s1; ++seq) {
-        const int n = seqlens[seq];
+        const int n = min(seqlens[seq], kMaxSeqLen);
         const int ks = seq == s0 ? t0 : 0;
         const int ke = seq == s1 ? t1 : n;
         if (ks >= ke) continue;
@@ -566,7 +566,10 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
         int pw_base = -1, pwin = 0;
         auto window_at = [&](int base) {
             pw_base = base;
-            pwin = base + lane <= pg_last ? bt_row[base + lane] : 0;
+            // columns past the table's width repeat its last one; entries
+            // outside the cache are clamped into it (negative ones too)
+            const int64_t col = min((int64_t)(base + lane), p.bt_stride - 1);
+            pwin = base + lane <= pg_last ? (int)min((uint32_t)bt_row[col], p.page_max) : 0;
         };
         auto page_of = [&](int T) {
             const int i = (T >> 1) - pw_base;

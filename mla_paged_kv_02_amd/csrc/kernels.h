@@ -12,6 +12,7 @@ struct DecodeParams {
     const uint16_t *kv;
     const int32_t *block_table;
     int64_t bt_stride;
+    uint32_t page_max;   // num_pages - 1: block-table entries are clamped to [0, page_max]
     const int32_t *seqlens;
     const int32_t *meta;
     int num_parts;
@@ -60,6 +61,10 @@ constexpr int kRowGroupsMax = 2048 / kCombineRows;   // s_q * h_q <= 16 * 128
 
 constexpr int kPartInts = 8;          // ints per scheduler-part record
 constexpr int kMetaMaxBatch = 8192;
+// Sequence lengths are capped at 2^21 tokens on the device, which keeps the
+// scheduler's chunk and cost sums (8192 sequences of 2^17 chunks, plus the
+// leads) inside int32.
+constexpr int kMaxSeqLen = 1 << 21;
 constexpr int kMaxParts = 65536;
 
 // Offsets (in int32) of the metadata sections for batch B and P parts:

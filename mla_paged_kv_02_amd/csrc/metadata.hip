@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *s
     // chunk and cost-unit counts, scanned together (cost = chunks + lead * non-empty)
     int local = 0, local_ne = 0;
     for (int b = b0; b < b1; ++b) {
-        const int n = max(seqlens[b], 0);
+        const int n = min(max(seqlens[b], 0), kMaxSeqLen);
         const int ch = (n + kChunk - 1) / kChunk;
         prefix[b] = ch;
         tail[b] = (unsigned char)(n - kChunk * (ch - 1));   // 1..16 (unused when ch == 0)

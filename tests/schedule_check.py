@@ -20,6 +20,11 @@ ROW_GROUPS_MAX = 512   # merge counters per heavy sequence
 
 
 WIDE_MIN_ROWS = 48
+MAX_SEQ_LEN = 1 << 21  # lengths are capped here on the device
+
+
+def capped(seqlens):
+    return np.clip(np.asarray(seqlens, dtype=np.int64), 0, MAX_SEQ_LEN)
 
 
 def lead_for(s_q, h_q):
@@ -31,7 +36,7 @@ def lead_for(s_q, h_q):
 
 
 def expected_metadata(seqlens, num_parts, lead):
-    n = np.maximum(np.asarray(seqlens, dtype=np.int64), 0)
+    n = capped(seqlens)
     B, P = len(n), int(num_parts)
     ch = (n + CHUNK - 1) // CHUNK
     # the unit list: (sequence, chunk index or -1 for a lead unit)
@@ -78,12 +83,13 @@ def expected_metadata(seqlens, num_parts, lead):
 
 def check_valid(meta, seqlens, num_parts):
     """Raise AssertionError unless the schedule covers each token once, in order."""
-    n = np.maximum(np.asarray(seqlens, dtype=np.int64), 0)
+    n = capped(seqlens)
     B, P = len(n), int(num_parts)
     meta = np.asarray(meta, dtype=np.int64)
     recs = meta[:8 * P].reshape(P, 8)
     split_off = meta[8 * P:8 * P + B + 1]
     assert split_off[0] == 0 and np.all(np.diff(split_off) >= 0)
+    assert split_off[-1] <= B + P, "more partial slots than the workspace holds"
     cursor = np.zeros(B, dtype=np.int64)        # next token expected per sequence
     slots_seen = [[] for _ in range(B)]
     last_seq = -1
