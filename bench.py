@@ -14,7 +14,10 @@ warmed by the previous one.
 
 Prints one JSON line.  Throughput is algorithmic bytes (Q + each attended
 cache row once per sequence + out + lse) per second; TFLOP/s uses
-2 * h_q * keys * (576 + 512).
+2 * h_q * keys * (576 + 512).  The roofline fraction is against the
+published MI355X peaks; `measured_peaks` adds what a plain streaming read
+and a dense bf16 MFMA loop reach on the same device, and the fraction of
+that.
 """
 from __future__ import annotations
 
@@ -55,6 +58,42 @@ WORKLOADS = {
                  "W_UK[128,128,512] bmm -> latent q (+64 rope) -> paged attention -> o_lat x "
                  "W_UV[128,512,128] bmm; bf16 N(0,1) activations and cache, N(0,0.02) weights",
 }
+
+
+def measured_peaks(mla, torch, dev, read_gib=2, mfma_iters=4096, reps=10):
+    """What this device reaches on a plain 16-byte streaming read of
+    read_gib GiB (2 workgroups per CU) and on a dense bf16 MFMA loop (four
+    workgroups of four waves per CU), medians of `reps` timed runs after two
+    warm-up runs."""
+    cus = mla.device_cus(dev.index or 0)
+    stream = torch.cuda.current_stream(dev)
+    buf = torch.empty(read_gib << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    wg_mfma = 4 * cus
+    fsink = torch.zeros(4 * wg_mfma, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        return float(np.median(ts))
+
+    t_read = timed(lambda: mla.probe_read(buf, 2 * cus, sink))
+    flops = mla.probe_mfma(mfma_iters, wg_mfma, fsink)
+    t_mfma = timed(lambda: mla.probe_mfma(mfma_iters, wg_mfma, fsink))
+    del buf
+    return {"hbm_read_GBs": round((read_gib << 30) / t_read / 1e9, 1),
+            "bf16_mfma_TFLOPs": round(flops / t_mfma / 1e12, 1),
+            "probe": "mla_probe_read over %d GiB, %d workgroups; mla_probe_mfma %d iters x 8 "
+                     "v_mfma_f32_32x32x16_bf16 per wave, %d workgroups of 4 waves"
+                     % (read_gib, 2 * cus, mfma_iters, wg_mfma)}
 
 
 def bmm_bytes_flops(batch, heads, k, n):
@@ -175,6 +214,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (no host launch cost)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the read and MFMA probes (measured peaks)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, five times (the known "
                          "byte count that scales the HBM traffic counters)")
@@ -318,7 +359,8 @@ def main():
     achieved = nbytes / (decode_ms / 1e3) / 1e9
     tflops = flops / (decode_ms / 1e3) / 1e12
     # the bound is whichever peak the workload's arithmetic intensity meets first
-    kernel = ("decode_wide_kernel" if (x.s_q * x.h_q) % 128 == 0 else "decode_r16_kernel")
+    rows = x.s_q * x.h_q
+    kernel = "decode_wide_kernel" if rows % 128 == 0 or rows >= 48 else "decode_r16_kernel"
     kernel = "mla_decode (%s + combine_kernel), HIP events" % kernel
     if flops / nbytes > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
         roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
@@ -359,6 +401,11 @@ def main():
     }
     if stages is not None:
         rec["stages"] = stages
+    if not args.no_peaks:
+        peaks = measured_peaks(mla, torch, dev)
+        ref = peaks["hbm_read_GBs"] if roofline["bound"] == "hbm" else peaks["bf16_mfma_TFLOPs"]
+        peaks["roofline_frac_of_measured"] = round(roofline["achieved"] / ref, 4)
+        rec["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

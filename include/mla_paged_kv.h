@@ -133,6 +133,11 @@ int mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int nu
  * the device) but keep every read inside the buffers: n is capped at 2^21
  * tokens, j/64 at bt_stride - 1 (keys past the table's width reuse its last
  * column) and an entry outside [0, num_pages) reads page num_pages - 1.
+ * With the environment variable MLA_DEBUG_CHECKS set (to anything but 0)
+ * the call first copies seqlens and block_table to host memory on `stream`,
+ * synchronizes it, and returns MLA_ERR_INVALID_ARG, launching nothing, if a
+ * length exceeds 64*bt_stride or 2^21 or a used entry is out of range (so
+ * the call is not capturable into a graph in that mode).
  *
  *   q           [device] bf16 [batch][s_q][h_q][576]
  *   kv_cache    [device] bf16 [num_pages][64][576]
@@ -194,6 +199,27 @@ int mla_absorb_bmm(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h,
                    const uint16_t *w, int heads, int K, int N,
                    uint16_t *y, int64_t y_stride_b, int64_t y_stride_h, int batch,
                    void *stream);
+
+/*
+ * Measurement probes: the rates this device reaches on the two resources
+ * the decode is bound by, so that achieved throughput can be quoted as a
+ * fraction of what is attainable as well as of the published peaks.
+ *
+ * mla_probe_read: streams `bytes` of `buf` once (16-byte loads, 16 KB
+ * contiguous per workgroup pass, `workgroups` workgroups of 256 threads
+ * striding over the buffer) and writes nothing unless the XOR
+ * of everything read hits one fixed 64-bit pattern (then sink[0]).
+ *   buf  [device] 16-byte aligned, bytes a positive multiple of 16
+ *   sink [device] uint32 [1]
+ * mla_probe_mfma: `workgroups` workgroups of four waves; every wave issues
+ * iters x 8 v_mfma_f32_32x32x16_bf16 (32768 flops each) on eight
+ * independent accumulators, i.e. workgroups * 4 * iters * 8 * 32768 flops,
+ * and writes one float per wave.
+ *   sink [device] float [workgroups * 4]
+ * Both are enqueued on `stream`; no device allocation.
+ */
+int mla_probe_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink, void *stream);
+int mla_probe_mfma(int iters, int workgroups, float *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,9 @@ MI355X (gfx950): a C-ABI library of hand-written HIP kernels
     out, lse = decode(q, kv_cache, block_table, seqlens, meta, parts, scale=s)
 """
 from .api import (absorb_bmm, combine, decode, default_num_parts, device_cus, get_metadata,
-                  metadata_ints, split_offsets, workspace_bytes)
+                  metadata_ints, probe_mfma, probe_read, split_offsets, workspace_bytes)
+from ._lib import MlaError
 
-__all__ = ["absorb_bmm", "combine", "decode", "default_num_parts", "device_cus", "get_metadata",
-           "metadata_ints", "split_offsets", "workspace_bytes"]
+__all__ = ["MlaError", "absorb_bmm", "combine", "decode", "default_num_parts", "device_cus",
+           "get_metadata", "metadata_ints", "probe_mfma", "probe_read", "split_offsets",
+           "workspace_bytes"]

@@ -174,3 +174,23 @@ def absorb_bmm(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = Non
                                           H, K, N, y.data_ptr(), y.stride(0), y.stride(1), B,
                                           _stream(x)), "mla_absorb_bmm")
     return y
+
+
+def probe_read(buf: torch.Tensor, workgroups: int, sink: Optional[torch.Tensor] = None) -> None:
+    """Stream every byte of `buf` (uint8, 16-byte multiple) once on the device."""
+    _need(buf, "buf", torch.uint8)
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _lib.check(_lib.load().mla_probe_read(buf.data_ptr(), buf.numel(), int(workgroups),
+                                          sink.data_ptr(), _stream(buf)), "mla_probe_read")
+
+
+def probe_mfma(iters: int, workgroups: int, sink: torch.Tensor) -> int:
+    """Run the dense bf16 MFMA loop; returns its flop count.  sink: float32
+    [workgroups * 4] on the device."""
+    _need(sink, "sink", torch.float32)
+    if sink.numel() < 4 * workgroups:
+        raise ValueError("sink needs %d floats" % (4 * workgroups))
+    _lib.check(_lib.load().mla_probe_mfma(int(iters), int(workgroups), sink.data_ptr(),
+                                          _stream(sink)), "mla_probe_mfma")
+    return int(workgroups) * 4 * int(iters) * 8 * 32768

@@ -11,6 +11,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <vector>
 
 #include "../../include/mla_paged_kv.h"
 #include "kernels.h"
@@ -54,6 +56,43 @@ int check_rows(int batch, int s_q, int h_q)
         return fail(MLA_ERR_UNSUPPORTED, "s_q must be in [1, %d] (got %d)", kMaxSq, s_q);
     if (!supported_heads(h_q))
         return fail(MLA_ERR_UNSUPPORTED, "h_q must be 16, 32, 64 or 128 (got %d)", h_q);
+    return MLA_OK;
+}
+
+// MLA_DEBUG_CHECKS set to a value other than 0: before launching, copy the
+// lengths and the block table to host memory (on the caller's stream, which
+// this synchronizes) and reject a length above 64 * bt_stride or 2^21 and a
+// used entry outside [0, num_pages).  Without it the kernels clamp such
+// values instead (every read stays inside the buffers, no error).
+bool debug_checks()
+{
+    const char *v = std::getenv("MLA_DEBUG_CHECKS");
+    return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
+}
+
+int check_tables(const int32_t *seqlens, const int32_t *block_table, int64_t bt_stride,
+                 int batch, int64_t num_pages, hipStream_t st)
+{
+    std::vector<int32_t> n((size_t)batch);
+    std::vector<int32_t> bt((size_t)batch * (size_t)bt_stride);
+    hipError_t e = hipMemcpyAsync(n.data(), seqlens, n.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(bt.data(), block_table, bt.size() * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_status(e, "debug check copy");
+    for (int b = 0; b < batch; ++b) {
+        if ((int64_t)n[b] > 64 * bt_stride || n[b] > mla::kMaxSeqLen)
+            return fail(MLA_ERR_INVALID_ARG,
+                        "seqlens[%d] = %d exceeds 64 * bt_stride = %lld or 2^21", b, n[b],
+                        (long long)(64 * bt_stride));
+        for (int64_t t = 0; t < ((int64_t)n[b] + 63) / 64; ++t) {
+            const int32_t page = bt[(size_t)b * (size_t)bt_stride + (size_t)t];
+            if (page < 0 || page >= num_pages)
+                return fail(MLA_ERR_INVALID_ARG,
+                            "block_table[%d][%lld] = %d is outside [0, %lld)", b, (long long)t,
+                            page, (long long)num_pages);
+        }
+    }
     return MLA_OK;
 }
 
@@ -160,11 +199,15 @@ int mla_decode(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
         return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu",
                     need, workspace == nullptr ? (size_t)0 : workspace_bytes);
 
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_checks())
+        if (int bad = check_tables(seqlens, block_table, bt_stride, batch, num_pages, st))
+            return bad;
+
     const int rows = s_q * h_q;
     const size_t slots = (size_t)batch + (size_t)num_parts;
     float *o_part = static_cast<float *>(workspace);
     float *lse_part = o_part + slots * (size_t)rows * 512;
-    hipStream_t st = static_cast<hipStream_t>(stream);
 
     mla::DecodeParams p;
     p.q = q;
@@ -265,6 +308,29 @@ int mla_absorb_bmm(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h,
     p.heads = heads;
     return hip_status(mla::launch_absorb(p, heads, static_cast<hipStream_t>(stream)),
                       "absorb kernel launch");
+}
+
+int mla_probe_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink, void *stream)
+{
+    if (!buf || !sink) return fail(MLA_ERR_INVALID_ARG, "buf and sink must be non-null");
+    if (bytes < 16 || bytes % 16 != 0 || !aligned(buf, 16))
+        return fail(MLA_ERR_INVALID_ARG, "buf must be 16-byte aligned and bytes a positive "
+                                         "multiple of 16");
+    if (workgroups < 1 || workgroups > (1 << 20))
+        return fail(MLA_ERR_INVALID_ARG, "workgroups must be in [1, 2^20]");
+    return hip_status(mla::launch_probe_read(buf, bytes, workgroups, sink,
+                                             static_cast<hipStream_t>(stream)),
+                      "read probe launch");
+}
+
+int mla_probe_mfma(int iters, int workgroups, float *sink, void *stream)
+{
+    if (!sink) return fail(MLA_ERR_INVALID_ARG, "sink must be non-null");
+    if (iters < 1 || workgroups < 1 || workgroups > (1 << 20))
+        return fail(MLA_ERR_INVALID_ARG, "iters must be >= 1 and workgroups in [1, 2^20]");
+    return hip_status(mla::launch_probe_mfma(iters, workgroups, sink,
+                                             static_cast<hipStream_t>(stream)),
+                      "mfma probe launch");
 }
 
 }  // extern "C"

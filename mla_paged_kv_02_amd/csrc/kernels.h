@@ -110,5 +110,8 @@ hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tile
 // `extra_wgs`: upper bound on the extra workgroups of the two-level merge
 hipError_t launch_combine(const CombineParams &p, int batch, int extra_wgs, hipStream_t stream);
 hipError_t launch_absorb(const AbsorbParams &p, int heads, hipStream_t stream);
+hipError_t launch_probe_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink,
+                             hipStream_t stream);
+hipError_t launch_probe_mfma(int iters, int workgroups, float *sink, hipStream_t stream);
 
 }  // namespace mla

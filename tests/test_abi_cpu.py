@@ -99,3 +99,8 @@ def test_other_validation(lib):
     assert lib.mla_absorb_bmm(FAKE, 0, 0, FAKE, 65535, 32, 6400, FAKE, 0, 0, 192, None) == \
         _lib.MLA_ERR_UNSUPPORTED
     assert lib.mla_device_cus(0, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_probe_read(FAKE, 100, 8, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_probe_read(FAKE + 8, 1 << 20, 8, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_probe_read(FAKE, 1 << 20, 0, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_probe_mfma(0, 8, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_probe_mfma(16, 8, None, None) == _lib.MLA_ERR_INVALID_ARG

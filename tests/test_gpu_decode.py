@@ -297,3 +297,28 @@ def test_metadata_at_the_largest_batch_and_lengths():
     m = meta.cpu().numpy()
     sc.check_valid(m, seqlens, parts)
     assert m[8 * parts + 8192 + 1] == 8192 * ((1 << 21) // 16)   # total chunks
+
+
+def test_debug_checks_reject_out_of_range_tables(monkeypatch):
+    """MLA_DEBUG_CHECKS=1: valid inputs (with -1 in the unused columns) give
+    the usual result; a used entry outside the cache or a length past the
+    table's width is an MLA_ERR_INVALID_ARG naming the offending value."""
+    x = gen.make_decode([200, 130, 77], s_q=1, h_q=16, causal=False, seed=33, poison=False)
+    assert np.any(x.block_table == -1)
+    d = gu.DeviceInputs(x)
+    monkeypatch.setenv("MLA_DEBUG_CHECKS", "1")
+    out, lse, _, _ = gu.run_decode(d)
+    ro, rl = gu.oracle_decode(x)
+    gu.compare(gu.dev_to_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl, "debug checks")
+    P = x.kv.shape[0]
+    for bad in (P, -1):
+        bt = x.block_table.copy()
+        bt[1, 1] = bad
+        d.bt = torch.from_numpy(bt).cuda()
+        with pytest.raises(mla.MlaError, match=r"block_table\[1\]\[1\]"):
+            gu.run_decode(d)
+    d.bt = torch.from_numpy(np.ascontiguousarray(x.block_table[:, :3])).cuda()
+    with pytest.raises(mla.MlaError, match=r"seqlens\[0\] = 200"):
+        gu.run_decode(d)
+    monkeypatch.setenv("MLA_DEBUG_CHECKS", "0")
+    gu.run_decode(d)   # checks off: the clamped read, no error
