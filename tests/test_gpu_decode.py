@@ -322,3 +322,35 @@ def test_debug_checks_reject_out_of_range_tables(monkeypatch):
         gu.run_decode(d)
     monkeypatch.setenv("MLA_DEBUG_CHECKS", "0")
     gu.run_decode(d)   # checks off: the clamped read, no error
+
+
+@pytest.mark.parametrize("name,num_parts", [("memory_bound", None), ("compute_bound", None),
+                                            ("skewed", None), ("tiny", 7)])
+def test_merge_reads_fresh_partials(name, num_parts):
+    """Split sequences' partials are written and read back inside every call
+    (the heavy sequence of the skewed workload also merged in two levels, in
+    place).  The workspace is filled with NaN before every other call and
+    with finite garbage in between, so a partial read before it was written,
+    or a stale one, shows up as a NaN or a changed bit; twenty calls must
+    give bitwise the same result, and leave the merge counters at zero."""
+    x = gen.make_config(name)
+    d = gu.DeviceInputs(x)
+    meta, parts = mla.get_metadata(d.seqlens, x.s_q, x.h_q, num_parts)
+    ws = torch.empty(mla.workspace_bytes(x.batch, x.s_q, x.h_q, parts), dtype=torch.uint8,
+                     device="cuda")
+    ref = None
+    for i in range(20):
+        ws.view(torch.float32)[: ws.numel() // 4].fill_(float("nan") if i % 2 == 0 else 1e30)
+        out, lse = mla.decode(d.q, d.kv, d.bt, d.seqlens, meta, parts, scale=x.scale,
+                              causal=x.causal, workspace=ws)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out.float()).any(), "NaN in call %d" % i
+        if ref is None:
+            ref = (out.clone(), lse.clone())
+        else:
+            assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16)), "call %d" % i
+            assert torch.equal(lse, ref[1]), "call %d" % i
+    # the counters are back to zero: the metadata equals a fresh schedule
+    fresh, _ = mla.get_metadata(d.seqlens, x.s_q, x.h_q, parts)
+    torch.cuda.synchronize()
+    assert torch.equal(meta, fresh)
