@@ -38,6 +38,16 @@
  *   the up-projections are applied as sequential batched matmuls instead):
  *     y[b,h,n] = sum_k x[b,h,k] * W[h,k,n]
  *
+ *   FP8 weights for the absorption bmm (the same PR description: weights
+ *   stored in fp8 are decompressed to 16-bit floats before the bmm, since no
+ *   fp8 bmm is used).  The pages fix neither the fp8 format nor the scale
+ *   granularity; the reading taken here: OCP FP8 E4M3 codes (sign, 4-bit
+ *   exponent with bias 7, 3-bit mantissa; exponent field 0 holds the
+ *   subnormals m * 2^-9; S.1111.111 is NaN; no infinities) with one fp32
+ *   scale per 128 x 128 block of each head's K x N matrix, decompressed as
+ *     W[h,k,n] = bf16( e4m3(code[h,k,n]) * scale[h, k / 128, n / 128] )
+ *   where the product is exact and bf16() rounds it once, to nearest even.
+ *
  * Precision: inputs that are bf16 in the product (cache rows, weights) are
  * passed as raw bf16 bit patterns and widened exactly to fp64 here;
  * activations are passed as fp64.  All arithmetic is fp64 and nothing is
@@ -186,6 +196,58 @@ void oracle_combine(const double *o_parts, const double *lse_parts, int n_parts,
             for (int e = 0; e < d_v; ++e) orow[e] += w * op[e];
         }
     }
+}
+
+/* OCP FP8 E4M3 code to its exact value. */
+double oracle_e4m3_to_double(uint8_t code)
+{
+    const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);               /* subnormal: m * 2^-9 */
+    else v = ldexp(1.0 + m / 8.0, e - 7);                /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest bf16 (8 significant bits, fp32's exponent
+ * range, ties to even) and return its bit pattern. */
+uint16_t oracle_double_to_bf16(double x)
+{
+    if (isnan(x)) return 0x7FC0;
+    const int neg = signbit(x);
+    double a = fabs(x), r;
+    if (a == 0.0) return neg ? 0x8000 : 0;
+    int e;
+    frexp(a, &e);                       /* a = f * 2^e, f in [0.5, 1) */
+    if (e - 1 < -126) {
+        r = nearbyint(ldexp(a, 133)) * ldexp(1.0, -133);   /* subnormal step 2^-133 */
+    } else {
+        r = ldexp(nearbyint(ldexp(a, 8 - e)), e - 8);       /* 8 significant bits */
+    }
+    if (r >= ldexp(1.0, 128)) return neg ? 0xFF80 : 0x7F80;  /* overflow: infinity */
+    float f = (float)r;                 /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)((u >> 16) | (neg ? 0x8000u : 0u));
+}
+
+/*
+ * Decompress block-scaled fp8 weights to bf16 bits.
+ *   code  [heads][K][N] E4M3 codes
+ *   scale [heads][ceil(K / blk)][ceil(N / blk)] fp32
+ *   w     [heads][K][N] bf16 bits (output)
+ */
+void oracle_dequant_fp8(const uint8_t *code, const float *scale, int heads, int K, int N,
+                        int blk, uint16_t *w)
+{
+    const int kb = (K + blk - 1) / blk, nb = (N + blk - 1) / blk;
+    for (int h = 0; h < heads; ++h)
+        for (int k = 0; k < K; ++k)
+            for (int n = 0; n < N; ++n) {
+                const int64_t i = ((int64_t)h * K + k) * N + n;
+                const double sc = scale[((int64_t)h * kb + k / blk) * nb + n / blk];
+                w[i] = oracle_double_to_bf16(oracle_e4m3_to_double(code[i]) * sc);
+            }
 }
 
 /*

@@ -46,6 +46,12 @@ def bind(lib):
     lib.oracle_combine.argtypes = [P, P, i32, i64, i32, P, P]
     lib.oracle_absorb_bmm.restype = None
     lib.oracle_absorb_bmm.argtypes = [P, P, i32, i32, i32, i32, P]
+    lib.oracle_e4m3_to_double.restype = ctypes.c_double
+    lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_dequant_fp8.restype = None
+    lib.oracle_dequant_fp8.argtypes = [P, P, i32, i32, i32, i32, P]
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -143,6 +149,39 @@ def absorb_bmm(x, w_bits):
     y = np.zeros((B, H, N), dtype=np.float64)
     lib.oracle_absorb_bmm(_ptr(x), _ptr(w), B, H, K, N, _ptr(y))
     return y
+
+
+FP8_BLOCK = 128
+
+
+def e4m3_to_f64(code: int) -> float:
+    """Exact value of one OCP FP8 E4M3 code."""
+    return float(_load().oracle_e4m3_to_double(int(code)))
+
+
+def f64_to_bf16(x: float) -> int:
+    """Bit pattern of the bf16 nearest to x (ties to even)."""
+    return int(_load().oracle_double_to_bf16(float(x)))
+
+
+def dequant_fp8(codes, scales, blk: int = FP8_BLOCK):
+    """Decompress E4M3 weights to bf16 bits: W = bf16(e4m3(code) * scale of its
+    blk x blk block).  codes uint8 [H, K, N], scales fp32 [H, ceil(K/blk),
+    ceil(N/blk)]."""
+    lib = _load()
+    q = np.ascontiguousarray(codes, dtype=np.uint8)
+    sc = np.ascontiguousarray(scales, dtype=np.float32)
+    H, K, N = q.shape
+    assert sc.shape == (H, -(-K // blk), -(-N // blk)), sc.shape
+    w = np.zeros((H, K, N), dtype=np.uint16)
+    lib.oracle_dequant_fp8(_ptr(q), _ptr(sc), H, K, N, blk, _ptr(w))
+    return w
+
+
+def absorb_bmm_fp8(x, codes, scales, blk: int = FP8_BLOCK):
+    """The absorption bmm with block-scaled fp8 weights decompressed to bf16
+    first (fp64 product of x and the bf16 weights)."""
+    return absorb_bmm(x, dequant_fp8(codes, scales, blk))
 
 
 def full_step(q_nope_bits, q_rope_bits, w_uk_bits, w_uv_bits, kv_bits, block_table,

@@ -36,6 +36,19 @@ MUTANTS = {
     "query_of_wrong_head": ("const double *qrow = q + r * d_qk;",
                             "const double *qrow = q + (r - r % h_q) * d_qk;"),
     "mask_ignored_with_range": ("if (hi > L) hi = L;", "if (hi > n) hi = n;"),
+    "e4m3_bias_8": ("else v = ldexp(1.0 + m / 8.0, e - 7);", "else v = ldexp(1.0 + m / 8.0, e - 8);"),
+    "e4m3_subnormal_scale": ("if (e == 0) v = ldexp((double)m, -9);",
+                             "if (e == 0) v = ldexp((double)m, -10);"),
+    "e4m3_mantissa_bits": ("else v = ldexp(1.0 + m / 8.0, e - 7);",
+                           "else v = ldexp(1.0 + m / 16.0, e - 7);"),
+    "bf16_truncates": ("r = ldexp(nearbyint(ldexp(a, 8 - e)), e - 8);",
+                       "r = ldexp(floor(ldexp(a, 8 - e)), e - 8);"),
+    "bf16_seven_bits": ("r = ldexp(nearbyint(ldexp(a, 8 - e)), e - 8);",
+                        "r = ldexp(nearbyint(ldexp(a, 7 - e)), e - 7);"),
+    "fp8_block_index_swapped": ("scale[((int64_t)h * kb + k / blk) * nb + n / blk]",
+                                "scale[((int64_t)h * kb + (n / blk) % kb) * nb + (k / blk) % nb]"),
+    "fp8_block_of_wrong_head": ("scale[((int64_t)h * kb + k / blk) * nb + n / blk]",
+                                "scale[(k / blk) * nb + n / blk]"),
 }
 
 PINS = [
@@ -48,6 +61,10 @@ PINS = [
     lambda: pins.test_causal_row_equals_shorter_decode(),
     lambda: pins.test_absorb_bmm_bruteforce(),
     lambda: pins.test_empty_rows(),
+    lambda: pins.test_e4m3_known_codes(),
+    lambda: pins.test_e4m3_code_structure(),
+    lambda: pins.test_bf16_rounding_of_exact_products(),
+    lambda: pins.test_dequant_block_scales_land_on_their_blocks(),
 ]
 
 

@@ -294,3 +294,101 @@ def test_bad_block_table_is_reported():
     bt[0, 1] = x.kv.shape[0]
     with pytest.raises(ValueError):
         orc.attend(x.q, x.kv, bt, x.seqlens, s_q=1, h_q=16, scale=x.scale, causal=False)
+
+
+# ---- fp8 weights: OCP FP8 E4M3 codes with one fp32 scale per 128 x 128 block,
+# decompressed to bf16 before the bmm (the reading stated in the oracle of the
+# absorption PR's "fp8 weights decompressed to 16-bit floats").
+
+# Values the E4M3 format fixes (sign, exponent bias 7, 3 mantissa bits,
+# subnormals m * 2^-9, max normal S.1111.110, NaN S.1111.111).
+E4M3_KNOWN = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+              0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x3C: 1.5, 0x40: 2.0, 0x70: 128.0,
+              0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+
+
+def test_e4m3_known_codes():
+    for code, v in E4M3_KNOWN.items():
+        assert orc.e4m3_to_f64(code) == v, hex(code)
+    assert math.copysign(1.0, orc.e4m3_to_f64(0x80)) == -1.0 and orc.e4m3_to_f64(0x80) == 0.0
+    assert math.isnan(orc.e4m3_to_f64(0x7F)) and math.isnan(orc.e4m3_to_f64(0xFF))
+
+
+def test_e4m3_code_structure():
+    """Positive codes increase with the code; inside a binade (exponent field
+    e >= 1) neighbours are 2^(e - 10) apart, subnormals 2^-9; negative codes
+    mirror; the only NaNs are 0x7F and 0xFF."""
+    v = [orc.e4m3_to_f64(c) for c in range(256)]
+    assert [c for c in range(256) if math.isnan(v[c])] == [0x7F, 0xFF]
+    for c in range(0x7E):
+        e = c >> 3
+        step = 2.0 ** (e - 10) if e >= 1 else 2.0 ** -9
+        assert v[c + 1] - v[c] == step, hex(c)   # also across binade edges
+    for c in range(0x7F):
+        assert v[c | 0x80] == -v[c]
+
+
+def _bf16_exact_rne(x: float) -> float:
+    """Nearest value with 8 significant bits (ties to even), by exact
+    rational arithmetic -- normal range only."""
+    from fractions import Fraction
+    f = Fraction(x)
+    if f == 0:
+        return 0.0
+    sign = -1 if f < 0 else 1
+    f = abs(f)
+    e = math.floor(math.log2(f))
+    while Fraction(2) ** e > f:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= f:
+        e += 1
+    unit = Fraction(2) ** (e - 7)
+    q, r = divmod(f, unit)
+    if r * 2 > unit or (r * 2 == unit and q % 2 == 1):
+        q += 1
+    return sign * float(q * unit)
+
+
+def test_bf16_rounding_of_exact_products():
+    """The decompression rounds e4m3 * scale once: ties go to even, and 500
+    random products round as exact rational arithmetic says."""
+    def val(bits):
+        return float(gen.bf16_bits_to_f32(np.array([bits], dtype=np.uint16))[0])
+    assert orc.f64_to_bf16(1 + 2.0 ** -8) == 0x3F80          # tie -> even (1.0)
+    assert orc.f64_to_bf16(1 + 3 * 2.0 ** -8) == 0x3F82      # tie -> even (1 + 2^-6)
+    assert orc.f64_to_bf16(-(1 + 2.0 ** -8)) == 0xBF80
+    assert orc.f64_to_bf16(2.0 ** -133) == 0x0001            # smallest subnormal
+    assert orc.f64_to_bf16(2.0 ** -134) == 0x0000            # half of it: tie -> even 0
+    assert orc.f64_to_bf16(2.0 ** 128) == 0x7F80             # overflow -> infinity
+    rng = np.random.default_rng(11)
+    for _ in range(500):
+        code = int(rng.integers(0, 256))
+        if code & 0x7F == 0x7F:
+            continue
+        sc = float(np.float32(rng.uniform(1e-5, 1e-2)))
+        x = orc.e4m3_to_f64(code) * sc
+        assert val(orc.f64_to_bf16(x)) == _bf16_exact_rne(x), (hex(code), sc)
+
+
+def test_dequant_block_scales_land_on_their_blocks():
+    """2 heads of 256 x 384 (2 x 3 blocks, not square): with scale 1 every
+    weight is its code's value (exact in bf16); with block (h, i, j) scaled
+    by 2^-(6h + 3i + j) every weight of that block is scaled exactly so.  A
+    swapped or mis-strided block index fails."""
+    rng = np.random.default_rng(12)
+    codes = rng.integers(0, 256, size=(2, 256, 384)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    ones = np.ones((2, 2, 3), dtype=np.float32)
+    w1 = gen.bf16_bits_to_f32(orc.dequant_fp8(codes, ones)).astype(np.float64)
+    table = np.array([orc.e4m3_to_f64(c) for c in range(256)])
+    assert np.array_equal(w1, table[codes])
+    sc = np.array([[[2.0 ** -(6 * h + 3 * i + j) for j in range(3)] for i in range(2)]
+                   for h in range(2)], dtype=np.float32)
+    w2 = gen.bf16_bits_to_f32(orc.dequant_fp8(codes, sc)).astype(np.float64)
+    for h in range(2):
+        for i in range(2):
+            for j in range(3):
+                blk = (h, slice(128 * i, 128 * i + 128), slice(128 * j, 128 * j + 128))
+                assert np.array_equal(w2[blk], w1[blk] * sc[h, i, j]), (h, i, j)
+    for code, v in E4M3_KNOWN.items():
+        assert table[code] == v
