@@ -57,6 +57,8 @@ WORKLOADS = {
     "full_step": "batch 128, h 128, 8192 tokens each, page 64, shuffled pages; q_nope [.,128] x "
                  "W_UK[128,128,512] bmm -> latent q (+64 rope) -> paged attention -> o_lat x "
                  "W_UV[128,512,128] bmm; bf16 N(0,1) activations and cache, N(0,0.02) weights",
+    "full_step_fp8": "full_step with W_UK and W_UV stored as fp8 (OCP E4M3 codes, one fp32 "
+                     "scale per 128x128 block) and decompressed to bf16 inside the bmm kernels",
 }
 
 
@@ -96,9 +98,13 @@ def measured_peaks(mla, torch, dev, read_gib=2, mfma_iters=4096, reps=10):
                      % (read_gib, 2 * cus, mfma_iters, wg_mfma)}
 
 
-def bmm_bytes_flops(batch, heads, k, n):
-    """One absorbed-weight bmm y[b,h,:] = x[b,h,:] . W[h] (x, W, y bf16)."""
-    return (batch * heads * k + heads * k * n + batch * heads * n) * 2, 2 * batch * heads * k * n
+def bmm_bytes_flops(batch, heads, k, n, fp8w=False):
+    """One absorbed-weight bmm y[b,h,:] = x[b,h,:] . W[h]: x and y bf16, W bf16
+    or (fp8w) one-byte codes plus an fp32 scale per 128 x 128 block."""
+    w = heads * k * n * (1 if fp8w else 2)
+    if fp8w:
+        w += heads * -(-k // 128) * -(-n // 128) * 4
+    return (batch * heads * k + batch * heads * n) * 2 + w, 2 * batch * heads * k * n
 
 
 def pctl(v):
@@ -130,27 +136,33 @@ def cpu_baseline(x, min_seconds: float):
     many as fit the time."""
     from oracle import oracle as orc
     threads = orc.max_threads()
-    if x.name == "full_step":
+    if x.name in ("full_step", "full_step_fp8"):
         e = x.extra
+        fp8w = x.name == "full_step_fp8"
+        if fp8w:   # decompressed once, outside the timed chain
+            w_uk = orc.dequant_fp8(e["w_uk_fp8"], e["w_uk_scale"])
+            w_uv = orc.dequant_fp8(e["w_uv_fp8"], e["w_uv_scale"])
+        else:
+            w_uk, w_uv = e["w_uk"], e["w_uv"]
         done, t_all, k = 0, 0.0, 1
         t_end = time.perf_counter() + min_seconds
         while done < x.batch and time.perf_counter() < t_end:
             k = min(k, x.batch - done)
             sel = np.arange(done, done + k)
             t0 = time.perf_counter()
-            orc.full_step(e["q_nope"][sel], e["q_rope"][sel], e["w_uk"], e["w_uv"], x.kv,
+            orc.full_step(e["q_nope"][sel], e["q_rope"][sel], w_uk, w_uv, x.kv,
                           x.block_table[sel], x.seqlens[sel], scale=x.scale)
             t_all += time.perf_counter() - t0
             done += k
             k *= 2
         sl = x.seqlens[:done]
-        b1, _ = bmm_bytes_flops(done, x.h_q, 128, D_V)
-        b2, _ = bmm_bytes_flops(done, x.h_q, D_V, 128)
+        b1, _ = bmm_bytes_flops(done, x.h_q, 128, D_V, fp8w)
+        b2, _ = bmm_bytes_flops(done, x.h_q, D_V, 128, fp8w)
         nb = b1 + algorithmic_bytes(sl, 1, x.h_q) + b2
         return {"value": round(nb / t_all / 1e9, 3), "unit": "GB/s", "cores": threads,
                 "kind": "oracle",
-                "sample": "full_step chain (fp64) on the first %d of %d sequences, %.2f s"
-                          % (done, x.batch, t_all)}
+                "sample": "%s chain (fp64) on the first %d of %d sequences, %.2f s"
+                          % (x.name, done, x.batch, t_all)}
     times = []
     t_end = time.perf_counter() + min_seconds
     while True:
@@ -260,12 +272,31 @@ def main():
     out = torch.empty((x.batch, x.s_q, x.h_q, D_V), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((x.batch, x.s_q, x.h_q), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    full = args.config == "full_step"
+    full = args.config in ("full_step", "full_step_fp8")
+    fp8w = args.config == "full_step_fp8"
     if full:
         q_nope = to_dev(x.extra["q_nope"])
-        w_uk = to_dev(x.extra["w_uk"])
-        w_uv = to_dev(x.extra["w_uv"])
         y = torch.empty((x.batch, x.h_q, 128), dtype=torch.bfloat16, device=dev)
+        if fp8w:
+            w_uk8 = torch.from_numpy(x.extra["w_uk_fp8"]).to(dev)
+            w_uk_sc = torch.from_numpy(x.extra["w_uk_scale"]).to(dev)
+            w_uv8 = torch.from_numpy(x.extra["w_uv_fp8"]).to(dev)
+            w_uv_sc = torch.from_numpy(x.extra["w_uv_scale"]).to(dev)
+        else:
+            w_uk = to_dev(x.extra["w_uk"])
+            w_uv = to_dev(x.extra["w_uv"])
+
+    def bmm_uk():
+        if fp8w:
+            mla.absorb_bmm_fp8w(q_nope, w_uk8, w_uk_sc, q[:, 0, :, :D_V])
+        else:
+            mla.absorb_bmm(q_nope, w_uk, q[:, 0, :, :D_V])
+
+    def bmm_uv():
+        if fp8w:
+            mla.absorb_bmm_fp8w(out[:, 0], w_uv8, w_uv_sc, y)
+        else:
+            mla.absorb_bmm(out[:, 0], w_uv, y)
 
     # events: [start, after metadata, after W_UK bmm, after decode, after W_UV bmm]
     def step(i, ev=None):
@@ -275,7 +306,7 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if full:
-            mla.absorb_bmm(q_nope, w_uk, q[:, 0, :, :D_V])
+            bmm_uk()
         if ev is not None:
             ev[2].record(stream)
         mla.decode(q, kvs[i % replicas], bt, seqlens, meta, parts, scale=x.scale,
@@ -283,7 +314,7 @@ def main():
         if ev is not None:
             ev[3].record(stream)
         if full:
-            mla.absorb_bmm(out[:, 0], w_uv, y)
+            bmm_uv()
         if ev is not None:
             ev[4].record(stream)
 
@@ -336,8 +367,8 @@ def main():
     stages = None
     step_bytes, step_flops = nbytes, flops
     if full:
-        b1, f1 = bmm_bytes_flops(x.batch, x.h_q, 128, D_V)
-        b2, f2 = bmm_bytes_flops(x.batch, x.h_q, D_V, 128)
+        b1, f1 = bmm_bytes_flops(x.batch, x.h_q, 128, D_V, fp8w)
+        b2, f2 = bmm_bytes_flops(x.batch, x.h_q, D_V, 128, fp8w)
         st_uk = pctl([e[1].elapsed_time(e[2]) for e in events])
         st_uv = pctl([e[3].elapsed_time(e[4]) for e in events])
         st_all = pctl([e[0].elapsed_time(e[4]) for e in events])

@@ -201,6 +201,28 @@ int mla_absorb_bmm(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h,
                    void *stream);
 
 /*
+ * The same bmm with fp8 weights decompressed to bf16 inside the kernel (the
+ * absorption PR stores the weights in fp8 and decompresses them to 16-bit
+ * floats for the bmm, there being no fp8 bmm).  The format and the scale
+ * granularity are not on the pages; this library reads them as OCP FP8 E4M3
+ * codes (sign, 4-bit exponent with bias 7, 3-bit mantissa, subnormals,
+ * S.1111.111 = NaN) with one fp32 scale per 128 x 128 block of each head's
+ * K x N matrix:
+ *   W[h, k, n] = bf16( e4m3(w[h, k, n]) * w_scale[h, k / 128, n / 128] )
+ * (the exact product rounded once to nearest even), then y = x . W as in
+ * mla_absorb_bmm (fp32 accumulate, bf16 out).
+ *   w       [device] uint8 [heads][K][N] E4M3 codes, 16-byte aligned
+ *   w_scale [device] fp32 [heads][ceil(K / 128)][ceil(N / 128)]
+ * Other arguments, limits and errors as for mla_absorb_bmm.  Half the
+ * weight bytes of the bf16 path.  No device allocation; enqueued on
+ * `stream`.
+ */
+int mla_absorb_bmm_fp8w(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h,
+                        const uint8_t *w, const float *w_scale, int heads, int K, int N,
+                        uint16_t *y, int64_t y_stride_b, int64_t y_stride_h, int batch,
+                        void *stream);
+
+/*
  * Measurement probes: the rates this device reaches on the two resources
  * the decode is bound by, so that achieved throughput can be quoted as a
  * fraction of what is attainable as well as of the published peaks.

@@ -13,7 +13,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_page
 # exported symbols, in header order
 SYMBOLS = ("mla_status_str", "mla_last_error", "mla_device_cus", "mla_default_num_parts",
            "mla_metadata_ints", "mla_workspace_bytes", "mla_get_metadata", "mla_decode",
-           "mla_combine", "mla_absorb_bmm", "mla_probe_read", "mla_probe_mfma")
+           "mla_combine", "mla_absorb_bmm", "mla_absorb_bmm_fp8w", "mla_probe_read",
+           "mla_probe_mfma")
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARG = 1
@@ -61,6 +62,8 @@ def load() -> ctypes.CDLL:
     lib.mla_combine.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P]
     lib.mla_absorb_bmm.restype = i32
     lib.mla_absorb_bmm.argtypes = [P, i64, i64, P, i32, i32, i32, P, i64, i64, i32, P]
+    lib.mla_absorb_bmm_fp8w.restype = i32
+    lib.mla_absorb_bmm_fp8w.argtypes = [P, i64, i64, P, P, i32, i32, i32, P, i64, i64, i32, P]
     lib.mla_probe_read.restype = i32
     lib.mla_probe_read.argtypes = [P, i64, i32, P, P]
     lib.mla_probe_mfma.restype = i32

@@ -176,6 +176,34 @@ def absorb_bmm(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = Non
     return y
 
 
+def absorb_bmm_fp8w(x: torch.Tensor, w: torch.Tensor, w_scale: torch.Tensor,
+                    y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """absorb_bmm with fp8 weights: w [H, K, N] uint8 E4M3 codes (contiguous),
+    w_scale [H, ceil(K/128), ceil(N/128)] float32 (one scale per 128 x 128
+    block), decompressed to bf16 inside the kernel."""
+    dev = x.device
+    _need(x, "x", torch.bfloat16, contiguous=False)
+    _need(w, "w", torch.uint8, dev)
+    _need(w_scale, "w_scale", torch.float32, dev)
+    if x.dim() != 3 or w.dim() != 3 or w_scale.dim() != 3:
+        raise ValueError("x must be [B, H, K], w [H, K, N] and w_scale 3-D")
+    B, H, K = x.shape
+    if w.shape[0] != H or w.shape[1] != K:
+        raise ValueError("w must be [H=%d, K=%d, N]" % (H, K))
+    N = w.shape[2]
+    if tuple(w_scale.shape) != (H, -(-K // 128), -(-N // 128)):
+        raise ValueError("w_scale must be [%d, %d, %d]" % (H, -(-K // 128), -(-N // 128)))
+    if y is None:
+        y = torch.empty((B, H, N), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, dev, contiguous=False)
+    if tuple(y.shape) != (B, H, N) or y.stride(2) != 1 or x.stride(2) != 1:
+        raise ValueError("x and y need unit stride in their last dim and y shape [B, H, N]")
+    _lib.check(_lib.load().mla_absorb_bmm_fp8w(
+        x.data_ptr(), x.stride(0), x.stride(1), w.data_ptr(), w_scale.data_ptr(), H, K, N,
+        y.data_ptr(), y.stride(0), y.stride(1), B, _stream(x)), "mla_absorb_bmm_fp8w")
+    return y
+
+
 def probe_read(buf: torch.Tensor, workgroups: int, sink: Optional[torch.Tensor] = None) -> None:
     """Stream every byte of `buf` (uint8, 16-byte multiple) once on the device."""
     _need(buf, "buf", torch.uint8)

@@ -96,6 +96,44 @@ int check_tables(const int32_t *seqlens, const int32_t *block_table, int64_t bt_
     return MLA_OK;
 }
 
+// The per-head bmm behind both absorb entry points: bf16 weights w, or E4M3
+// weights w8 with their block scales.
+int absorb(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h, const uint16_t *w,
+           const uint8_t *w8, const float *wscale, int heads, int K, int N, uint16_t *y,
+           int64_t y_stride_b, int64_t y_stride_h, int batch, void *stream)
+{
+    if (!x || !y) return fail(MLA_ERR_INVALID_ARG, "x and y must be non-null");
+    if (batch < 1 || heads < 1) return fail(MLA_ERR_INVALID_ARG, "batch and heads must be >= 1");
+    if (K < 32 || K % 32 != 0 || N < 64 || N % 64 != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "K must be a multiple of 32 and N of 64 (got %d, %d)", K,
+                    N);
+    if (heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "heads must be <= 65535");
+    if ((int64_t)((heads + 7) / 8 * 8) * (N / 64) * ((batch + 63) / 64) >= (int64_t)1 << 24)
+        return fail(MLA_ERR_UNSUPPORTED, "too many (head, tile) workgroups: %d heads, N %d, batch %d",
+                    heads, N, batch);
+    if (x_stride_b % 8 || x_stride_h % 8 || y_stride_b % 8 || y_stride_h % 8 ||
+        x_stride_b < 0 || x_stride_h < 0 || y_stride_b < 0 || y_stride_h < 0)
+        return fail(MLA_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements");
+    if (!aligned(x, 16) || !aligned(y, 16))
+        return fail(MLA_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    mla::AbsorbParams p;
+    p.x = x;
+    p.x_sb = x_stride_b;
+    p.x_sh = x_stride_h;
+    p.w = w;
+    p.w8 = w8;
+    p.wscale = wscale;
+    p.K = K;
+    p.N = N;
+    p.y = y;
+    p.y_sb = y_stride_b;
+    p.y_sh = y_stride_h;
+    p.batch = batch;
+    p.heads = heads;
+    return hip_status(mla::launch_absorb(p, heads, static_cast<hipStream_t>(stream)),
+                      "absorb kernel launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -280,34 +318,22 @@ int mla_absorb_bmm(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h,
                    uint16_t *y, int64_t y_stride_b, int64_t y_stride_h, int batch,
                    void *stream)
 {
-    if (!x || !w || !y) return fail(MLA_ERR_INVALID_ARG, "x, w and y must be non-null");
-    if (batch < 1 || heads < 1) return fail(MLA_ERR_INVALID_ARG, "batch and heads must be >= 1");
-    if (K < 32 || K % 32 != 0 || N < 64 || N % 64 != 0)
-        return fail(MLA_ERR_UNSUPPORTED, "K must be a multiple of 32 and N of 64 (got %d, %d)", K,
-                    N);
-    if (heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "heads must be <= 65535");
-    if ((int64_t)((heads + 7) / 8 * 8) * (N / 64) * ((batch + 63) / 64) >= (int64_t)1 << 24)
-        return fail(MLA_ERR_UNSUPPORTED, "too many (head, tile) workgroups: %d heads, N %d, batch %d",
-                    heads, N, batch);
-    if (x_stride_b % 8 || x_stride_h % 8 || y_stride_b % 8 || y_stride_h % 8 ||
-        x_stride_b < 0 || x_stride_h < 0 || y_stride_b < 0 || y_stride_h < 0)
-        return fail(MLA_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements");
-    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16))
-        return fail(MLA_ERR_INVALID_ARG, "x, w and y must be 16-byte aligned");
-    mla::AbsorbParams p;
-    p.x = x;
-    p.x_sb = x_stride_b;
-    p.x_sh = x_stride_h;
-    p.w = w;
-    p.K = K;
-    p.N = N;
-    p.y = y;
-    p.y_sb = y_stride_b;
-    p.y_sh = y_stride_h;
-    p.batch = batch;
-    p.heads = heads;
-    return hip_status(mla::launch_absorb(p, heads, static_cast<hipStream_t>(stream)),
-                      "absorb kernel launch");
+    if (!w) return fail(MLA_ERR_INVALID_ARG, "w must be non-null");
+    if (!aligned(w, 16)) return fail(MLA_ERR_INVALID_ARG, "w must be 16-byte aligned");
+    return absorb(x, x_stride_b, x_stride_h, w, nullptr, nullptr, heads, K, N, y, y_stride_b,
+                  y_stride_h, batch, stream);
+}
+
+int mla_absorb_bmm_fp8w(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h,
+                        const uint8_t *w, const float *w_scale, int heads, int K, int N,
+                        uint16_t *y, int64_t y_stride_b, int64_t y_stride_h, int batch,
+                        void *stream)
+{
+    if (!w || !w_scale) return fail(MLA_ERR_INVALID_ARG, "w and w_scale must be non-null");
+    if (!aligned(w, 16) || !aligned(w_scale, 4))
+        return fail(MLA_ERR_INVALID_ARG, "w must be 16-byte aligned and w_scale 4-byte");
+    return absorb(x, x_stride_b, x_stride_h, nullptr, w, w_scale, heads, K, N, y, y_stride_b,
+                  y_stride_h, batch, stream);
 }
 
 int mla_probe_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink, void *stream)

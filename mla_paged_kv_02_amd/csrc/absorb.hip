@@ -20,6 +20,12 @@
 // of a head share an XCD (number L -> XCD L % 8, head L % 8 + 8 ((L / 8) /
 // tiles per head)), which keeps a head's x rows and W slabs in one L2
 // instead of fetching them from HBM once per XCD.
+//
+// The same PR stores the weights in fp8 and decompresses them to 16-bit
+// floats for the bmm.  With fp8 weights (OCP E4M3 codes, one fp32 scale per
+// 128 x 128 block) each thread loads 8 codes per slab instead of 8 bf16
+// (half the weight bytes) and decompresses them in registers before the LDS
+// stage; the rest of the kernel is the bf16 one.
 #include "mla_device.h"
 #include "kernels.h"
 
@@ -30,9 +36,32 @@ constexpr int kAbsBM = 64;              // batch rows per workgroup (16 per wave
 constexpr int kAbsBN = 64;              // output columns per workgroup
 constexpr int kAbsKSlab = 32;           // k rows per slab (one 16-byte load per thread)
 constexpr int kWStride = kAbsBN + 8;    // bf16 per staged row (144 B)
+constexpr int kFp8Block = 128;          // scale block of fp8 weights (k and n)
 
-
-template <int G>
+// fp8 weights: gfx950 decodes OCP E4M3 codes to fp32 exactly
+// (v_cvt_pk_f32_fp8).  The weight is bf16(code * scale), the exact product
+// rounded once to nearest even.  The fp32 product p = RN(code * scale) cannot
+// step over a bf16 rounding midpoint (midpoints are fp32 values), so
+// rounding p to bf16 (v_cvt_pk_bf16_f32, nearest even) is already right
+// unless p lies exactly on a midpoint while the exact product does not;
+// there the product's rounding error (exact, by fma) picks the side.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t round_scaled_bf16x2(float v0, float v1, float scale)
+{
+    const float p0 = v0 * scale, p1 = v1 * scale;
+    uint32_t r = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_v));
+    const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
+    if (__builtin_expect(((u0 & 0xFFFFu) == 0x8000u) | ((u1 & 0xFFFFu) == 0x8000u), 0)) {
+        const float e0 = __builtin_fmaf(v0, scale, -p0), e1 = __builtin_fmaf(v1, scale, -p1);
+        if ((u0 & 0xFFFFu) == 0x8000u && e0 != 0.f)
+            r = (r & 0xFFFF0000u) | ((((e0 > 0.f) == (p0 > 0.f)) ? u0 + 0x8000u : u0) >> 16);
+        if ((u1 & 0xFFFFu) == 0x8000u && e1 != 0.f)
+            r = (r & 0xFFFFu) | ((((e1 > 0.f) == (p1 > 0.f)) ? u1 + 0x8000u : u1) & 0xFFFF0000u);
+    }
+    return r;
+}
+template <int G, bool kFp8>
 __global__ __launch_bounds__(kAbsThreads) void absorb_kernel(AbsorbParams p)
 {
     __shared__ __attribute__((aligned(16))) short wt[G * kAbsKSlab * kWStride];
@@ -50,6 +79,11 @@ __global__ __launch_bounds__(kAbsThreads) void absorb_kernel(AbsorbParams p)
     const int m0 = (t / ntn) * kAbsBM;
 
     const uint16_t *wh = p.w + (int64_t)h * p.K * p.N;
+    const uint8_t *w8h = p.w8 + (int64_t)h * p.K * p.N;
+    const int kblocks = (p.K + kFp8Block - 1) / kFp8Block;
+    const int nblocks = (p.N + kFp8Block - 1) / kFp8Block;
+    // a 64-column tile lies inside one 128-column scale block
+    const float *sch = p.wscale + ((int64_t)h * kblocks) * nblocks + n0 / kFp8Block;
     const int brow = m0 + wave * 16 + r16;               // batch row of this lane (B operand)
     const bool row_ok = brow < p.batch;
     const uint16_t *xrow = p.x + (int64_t)(row_ok ? brow : 0) * p.x_sb + (int64_t)h * p.x_sh;
@@ -69,16 +103,39 @@ __global__ __launch_bounds__(kAbsThreads) void absorb_kernel(AbsorbParams p)
     for (int kg = 0; kg < p.K; kg += G * kAbsKSlab) {
         const int ns = min(G, (p.K - kg) / kAbsKSlab);   // slabs in this group (uniform)
         u32x4_t wv[G], xv[G];
+        u32x2_t wq[G];      // fp8: 8 codes per thread and slab
+        float wsc[G];       // fp8: the slab's scale (a 32-row slab lies in one block)
 #pragma unroll
         for (int s = 0; s < G; ++s) {
             wv[s] = u32x4_t{0u, 0u, 0u, 0u};
             xv[s] = u32x4_t{0u, 0u, 0u, 0u};
+            wq[s] = u32x2_t{0u, 0u};
+            wsc[s] = 0.f;
             if (s < ns) {
                 const int k0 = kg + s * kAbsKSlab;
-                wv[s] = *reinterpret_cast<const u32x4_t *>(wh + (int64_t)(k0 + srow) * p.N + n0 +
-                                                           scol);
+                if (kFp8) {
+                    wq[s] = *reinterpret_cast<const u32x2_t *>(w8h + (int64_t)(k0 + srow) * p.N +
+                                                               n0 + scol);
+                    wsc[s] = sch[(k0 / kFp8Block) * nblocks];
+                } else {
+                    wv[s] = *reinterpret_cast<const u32x4_t *>(wh + (int64_t)(k0 + srow) * p.N +
+                                                               n0 + scol);
+                }
                 if (row_ok) xv[s] = *reinterpret_cast<const u32x4_t *>(xrow + k0 + 8 * g);
             }
+        }
+        if (kFp8) {
+            // decompress to bf16 in registers, in the layout of the bf16 path
+            // (byte i of a word is code i; the pair form decodes bytes 0-1 or 2-3)
+#pragma unroll
+            for (int s = 0; s < G; ++s)
+#pragma unroll
+                for (int jw = 0; jw < 2; ++jw) {
+                    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wq[s][jw], false);
+                    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wq[s][jw], true);
+                    wv[s][2 * jw] = round_scaled_bf16x2(lo[0], lo[1], wsc[s]);
+                    wv[s][2 * jw + 1] = round_scaled_bf16x2(hi[0], hi[1], wsc[s]);
+                }
         }
         __syncthreads();   // the previous group fully consumed
 #pragma unroll
@@ -116,16 +173,24 @@ __global__ __launch_bounds__(kAbsThreads) void absorb_kernel(AbsorbParams p)
     }
 }
 
+template <int G>
+void launch_group(const AbsorbParams &p, dim3 grid, hipStream_t stream)
+{
+    if (p.w8 != nullptr)
+        hipLaunchKernelGGL((absorb_kernel<G, true>), grid, dim3(kAbsThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((absorb_kernel<G, false>), grid, dim3(kAbsThreads), 0, stream, p);
+}
+
 hipError_t launch_absorb(const AbsorbParams &p, int heads, hipStream_t stream)
 {
     const int tiles = (p.N / kAbsBN) * ((p.batch + kAbsBM - 1) / kAbsBM);
     const dim3 grid((unsigned)((heads + 7) / 8 * 8) * (unsigned)tiles);
-    if (p.K == 4 * kAbsKSlab)
-        hipLaunchKernelGGL(absorb_kernel<4>, grid, dim3(kAbsThreads), 0, stream, p);
-    else if (p.K == 16 * kAbsKSlab)
-        hipLaunchKernelGGL(absorb_kernel<16>, grid, dim3(kAbsThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(absorb_kernel<8>, grid, dim3(kAbsThreads), 0, stream, p);
+    // fp8 at K = 512: two groups of 8 slabs (the decompression of one group
+    // overlaps the other's loads; measured faster than one group of 16)
+    if (p.K == 4 * kAbsKSlab) launch_group<4>(p, grid, stream);
+    else if (p.K == 16 * kAbsKSlab && p.w8 == nullptr) launch_group<16>(p, grid, stream);
+    else launch_group<8>(p, grid, stream);
     return hipGetLastError();
 }
 

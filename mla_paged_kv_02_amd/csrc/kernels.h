@@ -44,7 +44,9 @@ struct CombineParams {
 struct AbsorbParams {
     const uint16_t *x;
     int64_t x_sb, x_sh;
-    const uint16_t *w;
+    const uint16_t *w;      // bf16 weights, or null when w8 is set
+    const uint8_t *w8;      // E4M3 weights [heads][K][N]
+    const float *wscale;    // their scales [heads][ceil(K/128)][ceil(N/128)]
     int K, N;
     uint16_t *y;
     int64_t y_sb, y_sh;

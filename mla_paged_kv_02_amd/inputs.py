@@ -16,6 +16,8 @@ description).  Every cache row is 576 bf16 values (512 latent + 64 rope).
   skewed         batch 32, s_q 1, h_q 16, one length 131072 and 31 of 1024
   full_step      batch 128, h 128, length 8192 each; q_nope [.,.,128],
                  W_UK [128,128,512], W_UV [128,512,128] ~ N(0, 0.02)
+  full_step_fp8  the same step with W_UK and W_UV stored as fp8 (E4M3 codes
+                 and one fp32 scale per 128 x 128 block, spread near 0.02)
 
 Wider query counts and the context-length sweep (the sequential-bmm PR
 measures serving at 1000, 5000, 10000 and 32000 input tokens; these decode
@@ -49,7 +51,7 @@ BF16_NAN = 0x7FC0
 
 CONFIG_INDEX = {"tiny": 0, "memory_bound": 1, "compute_bound": 2, "skewed": 3, "full_step": 4,
                 "multi_token_4": 5, "multi_token_8": 6, "len_1k": 7, "len_5k": 8, "len_10k": 9,
-                "len_32k": 10}
+                "len_32k": 10, "full_step_fp8": 11}
 SWEEP_LENGTHS = {"len_1k": 1000, "len_5k": 5000, "len_10k": 10000, "len_32k": 32000}
 
 
@@ -80,6 +82,23 @@ def normal_bf16(rng: np.random.Generator, shape, std: float = 1.0,
             v *= np.float32(std)
         out[s:e] = f32_to_bf16_bits(v)
     return out.reshape(shape)
+
+
+def fp8_weights(rng: np.random.Generator, shape, blk: int = 128, std: float = 0.02):
+    """Block-scaled fp8 weights as stored: E4M3 codes drawn as bit patterns
+    (random sign, exponent field around 10 -- about 8 -- clipped to [0, 15],
+    uniform mantissa; the NaN pattern S.1111.111 replaced by S.1111.110) and
+    one positive fp32 scale per blk x blk block of each [K, N] matrix, near
+    std / 16, so that code * scale has a standard deviation near std.  Returns (codes
+    uint8 [H, K, N], scales float32 [H, ceil(K/blk), ceil(N/blk)])."""
+    H, K, N = shape
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8)
+    expo = np.clip(np.rint(rng.normal(10.0, 1.0, size=shape)), 0, 15).astype(np.uint8)
+    mant = rng.integers(0, 8, size=shape, dtype=np.uint8)
+    mant[(expo == 15) & (mant == 7)] = 6
+    codes = (sign << 7) | (expo << 3) | mant
+    scales = (std / 16.0 * rng.uniform(0.5, 1.5, size=(H, -(-K // blk), -(-N // blk))))
+    return codes.astype(np.uint8), scales.astype(np.float32)
 
 
 @dataclass
@@ -115,7 +134,7 @@ def _lengths(name: str, rng: np.random.Generator) -> np.ndarray:
         n = np.full(32, 1024, dtype=np.int32)
         n[int(rng.integers(0, 32))] = 131072
         return n
-    if name == "full_step":
+    if name in ("full_step", "full_step_fp8"):
         return np.full(128, 8192, dtype=np.int32)
     if name in ("multi_token_4", "multi_token_8"):
         s_q = _SHAPES[name][0]
@@ -131,6 +150,7 @@ _SHAPES = {  # name -> (s_q, h_q, causal)
     "compute_bound": (2, 128, True),
     "skewed": (1, 16, False),
     "full_step": (1, 128, False),
+    "full_step_fp8": (1, 128, False),
     "multi_token_4": (4, 16, True),
     "multi_token_8": (8, 16, True),
     "len_1k": (1, 128, False),
@@ -198,17 +218,22 @@ def make_config(name: str, seed: Optional[int] = None) -> DecodeInputs:
     s_q, h_q, causal = _SHAPES[name]
     seqlens = _lengths(name, rng_len)
     kv, bt = paged_cache(seqlens, rng_perm, rng_kv)
-    if name == "full_step":
+    if name in ("full_step", "full_step_fp8"):
         B, H = len(seqlens), h_q
         q_nope = normal_bf16(rng_q, (B, H, 128))
         q_rope = normal_bf16(rng_q, (B, H, D_ROPE))
-        w_uk = normal_bf16(rng_w, (H, 128, D_V), std=0.02)
-        w_uv = normal_bf16(rng_w, (H, D_V, 128), std=0.02)
+        if name == "full_step":
+            extra = dict(w_uk=normal_bf16(rng_w, (H, 128, D_V), std=0.02),
+                         w_uv=normal_bf16(rng_w, (H, D_V, 128), std=0.02))
+        else:
+            uk, uk_s = fp8_weights(rng_w, (H, 128, D_V))
+            uv, uv_s = fp8_weights(rng_w, (H, D_V, 128))
+            extra = dict(w_uk_fp8=uk, w_uk_scale=uk_s, w_uv_fp8=uv, w_uv_scale=uv_s)
         q = np.zeros((B, 1, H, D_QK), dtype=np.uint16)
         q[:, 0, :, D_V:] = q_rope
         return DecodeInputs(q=q, kv=kv, block_table=bt, seqlens=seqlens, s_q=1, h_q=H,
                             causal=False, name=name,
-                            extra=dict(q_nope=q_nope, q_rope=q_rope, w_uk=w_uk, w_uv=w_uv))
+                            extra=dict(q_nope=q_nope, q_rope=q_rope, **extra))
     q = normal_bf16(rng_q, (len(seqlens), s_q, h_q, D_QK))
     return DecodeInputs(q=q, kv=kv, block_table=bt, seqlens=seqlens, s_q=s_q, h_q=h_q,
                         causal=causal, name=name)

@@ -19,7 +19,7 @@ FAKE = 0x10000   # aligned non-null address; never dereferenced (validation fail
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -99,6 +99,12 @@ def test_other_validation(lib):
     assert lib.mla_absorb_bmm(FAKE, 0, 0, FAKE, 65535, 32, 6400, FAKE, 0, 0, 192, None) == \
         _lib.MLA_ERR_UNSUPPORTED
     assert lib.mla_device_cus(0, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_bmm_fp8w(FAKE, 0, 0, FAKE, None, 4, 128, 64, FAKE, 0, 0, 2, None) == \
+        _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_bmm_fp8w(FAKE, 0, 0, FAKE, FAKE, 4, 100, 64, FAKE, 0, 0, 2, None) == \
+        _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_absorb_bmm_fp8w(FAKE, 0, 0, FAKE + 8, FAKE, 4, 128, 64, FAKE, 0, 0, 2,
+                                   None) == _lib.MLA_ERR_INVALID_ARG
     assert lib.mla_probe_read(FAKE, 100, 8, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
     assert lib.mla_probe_read(FAKE + 8, 1 << 20, 8, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
     assert lib.mla_probe_read(FAKE, 1 << 20, 0, FAKE, None) == _lib.MLA_ERR_INVALID_ARG

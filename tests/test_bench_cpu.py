@@ -39,6 +39,21 @@ def test_full_step_byte_and_flop_counts():
     assert flops == 2 * 128 * (128 * 8192) * (576 + 512)
 
 
+def test_fp8_weight_bytes():
+    """fp8 weights: one byte per weight plus an fp32 scale per 128 x 128 block;
+    activations stay bf16."""
+    b = _bench()
+    uk_b, uk_f = b.bmm_bytes_flops(128, 128, 128, 512, True)
+    assert uk_b == (128 * 128 * 128 + 128 * 128 * 512) * 2 + 128 * 128 * 512 + 128 * 1 * 4 * 4
+    assert uk_f == 2 * 128 * 128 * 128 * 512
+    uv_b, _ = b.bmm_bytes_flops(128, 128, 512, 128, True)
+    assert uv_b == (128 * 128 * 512 + 128 * 128 * 128) * 2 + 128 * 512 * 128 + 128 * 4 * 1 * 4
+    x = gen.make_config("full_step_fp8")
+    assert x.extra["w_uk_fp8"].shape == (128, 128, 512) and x.extra["w_uk_scale"].shape == (128, 1, 4)
+    assert x.extra["w_uv_fp8"].shape == (128, 512, 128) and x.extra["w_uv_scale"].shape == (128, 4, 1)
+    assert not np.any((x.extra["w_uk_fp8"] & 0x7F) == 0x7F)   # no NaN codes
+
+
 def test_causal_flops_count_each_query_row_once():
     """s_q = 2 causal: query i of a length-n sequence sees n - 1 + i keys."""
     b = _bench()

@@ -70,3 +70,74 @@ def test_full_step_sampled():
     got_o = gu.dev_to_f64(o_lat[:, 0])[sel]
     assert np.abs(got_o - ro).max() <= gu.MAX_ABS
     assert np.abs(lse.cpu().numpy()[sel, 0] - rl).max() <= 2e-3
+
+
+FP8_SHAPES = [(128, 8, 128, 512), (128, 8, 512, 128), (37, 3, 64, 64), (70, 5, 320, 128),
+              (9, 2, 1024, 64), (1, 2, 32, 192)]
+
+
+@pytest.mark.parametrize("B,H,K,N", FP8_SHAPES)
+def test_absorb_bmm_fp8w(B, H, K, N):
+    """fp8 weights (E4M3 codes, 128 x 128 block scales; partial blocks where K
+    or N is not a multiple of 128) against the oracle's decompression and
+    fp64 product."""
+    rng = np.random.default_rng(B * 11 + K)
+    x = gen.normal_bf16(rng, (B, H, K))
+    codes, scales = gen.fp8_weights(rng, (H, K, N))
+    y = mla.absorb_bmm_fp8w(gu.bits_to_dev(x), torch.from_numpy(codes).cuda(),
+                            torch.from_numpy(scales).cuda())
+    torch.cuda.synchronize()
+    got = gu.dev_to_f64(y)
+    ref = orc.absorb_bmm_fp8(x, codes, scales)
+    d = np.abs(got - ref)
+    assert d.max() <= gu.MAX_ABS and d.mean() <= gu.MEAN_ABS
+    assert _rel_l2(got, ref) <= 1e-2
+
+
+@pytest.mark.parametrize("B,H,K,N", FP8_SHAPES[:4])
+def test_absorb_bmm_fp8w_decompresses_like_the_oracle(B, H, K, N):
+    """The kernel's bf16 weights are the oracle's bit for bit (one rounding of
+    the exact product), so the fp8 path equals the bf16 path run on the
+    oracle's decompressed weights, bitwise.  Every non-NaN code (zeros,
+    subnormals, negatives, +-448) appears in the weights."""
+    rng = np.random.default_rng(B * 13 + N)
+    x = gu.bits_to_dev(gen.normal_bf16(rng, (B, H, K)))
+    codes, scales = gen.fp8_weights(rng, (H, K, N))
+    every = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    flat = codes.reshape(-1)
+    flat[rng.choice(flat.size, size=min(flat.size, 4 * every.size), replace=False)] = \
+        np.resize(every, min(flat.size, 4 * every.size))
+    y8 = mla.absorb_bmm_fp8w(x, torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
+    y16 = mla.absorb_bmm(x, gu.bits_to_dev(orc.dequant_fp8(codes, scales)))
+    torch.cuda.synchronize()
+    assert torch.equal(y8.view(torch.int16), y16.view(torch.int16))
+
+
+def test_full_step_fp8_sampled():
+    """The full decode step with fp8 W_UK and W_UV at batch 128, 128 heads,
+    8192 tokens each, against the fp64 chain on a sample of sequences."""
+    x = gen.make_config("full_step_fp8")
+    e = x.extra
+    d = gu.DeviceInputs(x)
+    H = x.h_q
+    q = d.q
+    mla.absorb_bmm_fp8w(gu.bits_to_dev(e["q_nope"]), torch.from_numpy(e["w_uk_fp8"]).cuda(),
+                        torch.from_numpy(e["w_uk_scale"]).cuda(), q[:, 0, :, :512])
+    meta, parts = mla.get_metadata(d.seqlens, 1, H)
+    o_lat, lse = mla.decode(q, d.kv, d.bt, d.seqlens, meta, parts, scale=x.scale)
+    y = mla.absorb_bmm_fp8w(o_lat[:, 0], torch.from_numpy(e["w_uv_fp8"]).cuda(),
+                            torch.from_numpy(e["w_uv_scale"]).cuda())
+    torch.cuda.synchronize()
+    sel = np.array([0, 57, 127])
+    w_uk = orc.dequant_fp8(e["w_uk_fp8"], e["w_uk_scale"])
+    w_uv = orc.dequant_fp8(e["w_uv_fp8"], e["w_uv_scale"])
+    _, o_ref, lse_ref, y_ref = orc.full_step(e["q_nope"][sel], e["q_rope"][sel], w_uk, w_uv,
+                                             x.kv, x.block_table[sel], x.seqlens[sel],
+                                             scale=x.scale)
+    got_y = gu.dev_to_f64(y)[sel]
+    d_y = np.abs(got_y - y_ref)
+    assert d_y.max() <= gu.MAX_ABS and d_y.mean() <= gu.MEAN_ABS
+    assert _rel_l2(got_y, y_ref) <= 1e-2
+    got_o = gu.dev_to_f64(o_lat[:, 0])[sel]
+    assert np.abs(got_o - o_ref).max() <= gu.MAX_ABS
+    assert np.abs(lse.cpu().numpy()[sel, 0] - lse_ref).max() <= 2e-3
