@@ -192,6 +192,12 @@ def source_digest():
     return h.hexdigest()
 
 
+def decode_kernel(rows):
+    """The decode kernel the library runs for s_q * h_q = rows: the 128-row
+    one for multiples of 128 and from 48 rows on, else the 16-row one."""
+    return "decode_wide_kernel" if rows % 128 == 0 or rows >= 48 else "decode_r16_kernel"
+
+
 def measured_traffic(config, x):
     """HBM bytes (fetched + written) of one mla_decode call (decode kernel +
     combine), from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
@@ -207,7 +213,7 @@ def measured_traffic(config, x):
     if rec.get("source_sha256") != source_digest() or config not in rec.get("per_launch", {}):
         return None
     k = rec["per_launch"][config]
-    decode = "decode_wide_kernel" if (x.s_q * x.h_q) % 128 == 0 else "decode_r16_kernel"
+    decode = decode_kernel(x.s_q * x.h_q)
     if decode not in k or "combine_kernel" not in k:
         return None
     return int(sum(k[n]["fetch_bytes"] + k[n]["write_bytes"] for n in (decode, "combine_kernel")))
@@ -390,9 +396,7 @@ def main():
     achieved = nbytes / (decode_ms / 1e3) / 1e9
     tflops = flops / (decode_ms / 1e3) / 1e12
     # the bound is whichever peak the workload's arithmetic intensity meets first
-    rows = x.s_q * x.h_q
-    kernel = "decode_wide_kernel" if rows % 128 == 0 or rows >= 48 else "decode_r16_kernel"
-    kernel = "mla_decode (%s + combine_kernel), HIP events" % kernel
+    kernel = "mla_decode (%s + combine_kernel), HIP events" % decode_kernel(x.s_q * x.h_q)
     if flops / nbytes > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
         roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
