@@ -102,8 +102,8 @@ size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts);
  * the sequence lengths on the device (no host synchronization) and cuts the
  * sequences, in batch order, into `num_parts` contiguous ranges of near-equal
  * cost, where a sequence costs its 16-token chunks plus a fixed lead of C
- * chunks for starting it (C = 8 when s_q * h_q >= 48, the 128-row kernel,
- * else 16): with TC cost units in all and U = min(num_parts, TC), part p < U takes
+ * chunks for starting it (with R = s_q * h_q: C = 8 when R = 128, 24 when
+ * R > 128, else 16): with TC cost units in all and U = min(num_parts, TC), part p < U takes
  * the chunks whose units fall in [floor(p*TC/U), floor((p+1)*TC/U)), chunk i
  * of sequence b sitting at unit (units of the sequences before b) + C + i.
  * A part whose range holds lead units only is empty.  Writes the metadata

@@ -106,7 +106,14 @@ constexpr int decode_row_tiles(int rows)
 {
     return use_wide(rows) ? (rows + kWideRows - 1) / kWideRows : (rows + 15) / 16;
 }
-constexpr int schedule_lead(int rows) { return use_wide(rows) ? 8 : 16; }
+// Lead cost (chunks) of starting a sequence, chosen per row count by
+// interleaved timing of the leads 8, 16, 24, 32: 16 for the 16-row kernel
+// and for partly empty 128-row tiles (fewer rows per chunk of work), 8 at
+// 128 rows, 24 from two row tiles on (both tiles of a part pay the start).
+constexpr int schedule_lead(int rows)
+{
+    return !use_wide(rows) ? 16 : rows < kWideRows ? 16 : rows == kWideRows ? 8 : 24;
+}
 hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tiles,
                               hipStream_t stream);
 // `extra_wgs`: upper bound on the extra workgroups of the two-level merge

@@ -11,7 +11,8 @@
 // [floor(p*TC/U), floor((p+1)*TC/U)); a part holds the chunks whose units
 // fall in its range (a range of lead-in units only makes an empty part), so a
 // part that starts a sequence gets C fewer chunks.  C is 16 chunks for the
-// 16-row kernel and 8 for the 128-row one (measured per-sequence overheads).
+// 16-row kernel and for 48..127 rows, 8 for 128 rows and 24 beyond (measured
+// per-sequence overheads; schedule_lead in kernels.h).
 // Chunk i of sequence b sits at unit cpre[b] + C + i, and the part owning
 // unit x is floor(((x+1)*U - 1) / TC).  A sequence touched by k parts gets k
 // partial-result slots (k = 1: written in place by the decode kernel).

@@ -19,7 +19,6 @@ HEAVY_CHUNK = 16       # splits per first-level merge workgroup
 ROW_GROUPS_MAX = 512   # merge counters per heavy sequence
 
 
-WIDE_MIN_ROWS = 48
 MAX_SEQ_LEN = 1 << 21  # lengths are capped here on the device
 
 
@@ -28,11 +27,11 @@ def capped(seqlens):
 
 
 def lead_for(s_q, h_q):
-    """Cost of starting a sequence, in chunks, for the kernel serving s_q*h_q
-    rows: 8 for the 128-row kernel (multiples of 128, or 48 rows and more),
-    16 for the 16-row kernel."""
+    """Cost of starting a sequence, in chunks, for s_q*h_q rows: 16 below 128
+    rows (the 16-row kernel, and partly empty 128-row tiles), 8 at exactly
+    128 rows, 24 above (two or more 128-row tiles)."""
     r = s_q * h_q
-    return 8 if (r % WIDE_ROWS == 0 or r >= WIDE_MIN_ROWS) else 16
+    return 16 if r < WIDE_ROWS else 8 if r == WIDE_ROWS else 24
 
 
 def expected_metadata(seqlens, num_parts, lead):
