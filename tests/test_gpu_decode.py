@@ -151,13 +151,17 @@ def test_constant_values_give_that_value():
     assert np.max(np.abs(got - want)) <= 2.0 ** -7 * 2
 
 
-def test_combine_entry_point():
+@pytest.mark.parametrize("n_parts", [4, 12, 40, 100])
+def test_combine_entry_point(n_parts):
     """mla_combine on oracle partials over random key splits equals the
-    unsplit oracle result."""
+    unsplit oracle result: up to 8 splits (one round trip), 9..32 (lse first,
+    rows eight at a time), more than 32 (the one-level merge with four waves
+    per row that the read-only entry point uses).  Random cut points leave
+    empty splits (lse -inf, weight 0), and the causal length-1 sequence has
+    a row with no visible key at all."""
     x = gen.make_decode([300, 65, 1, 129], s_q=2, h_q=16, causal=True, seed=12)
     from oracle import oracle as orc
-    rng = np.random.default_rng(5)
-    n_parts = 4
+    rng = np.random.default_rng(5 + n_parts)
     cuts = []
     for n in x.seqlens:
         c = np.sort(rng.integers(0, n + 1, n_parts - 1))
