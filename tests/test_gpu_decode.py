@@ -208,6 +208,17 @@ def test_forced_part_counts_several_row_tiles(s_q, h_q, num_parts):
     assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
 
 
+@pytest.mark.parametrize("num_parts", [None, 3, 40])
+def test_largest_row_count(num_parts):
+    """The largest query shape the interface takes: s_q 16 x h_q 128 = 2048
+    rows per sequence (16 row tiles of the 128-row kernel, 512 row groups in
+    the merge), causal, with empty and short sequences; the default part
+    count (16), and forced ones that split sequences several ways."""
+    x = gen.make_decode([0, 1, 17, 100, 700, 2049], s_q=16, h_q=128, causal=True, seed=77)
+    _, meta, parts = _check(x, num_parts=num_parts, what="2048 rows parts=%s" % num_parts)
+    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
+
+
 @pytest.mark.parametrize("s_q,h_q", [(2, 64), (4, 32), (8, 16), (2, 128)])
 def test_causal_multi_query_wide_rows(s_q, h_q):
     x = gen.make_decode([1, 2, 5, 31, 32, 33, 64, 97, 1000, 2049], s_q=s_q, h_q=h_q, causal=True,
