@@ -124,12 +124,21 @@ __device__ __forceinline__ void process_chunk(const ChunkRegs &k, const lds_shor
     const float e0 = fast_exp2(sv[0] - m_use), e1 = fast_exp2(sv[1] - m_use);
     const float e2 = fast_exp2(sv[2] - m_use), e3 = fast_exp2(sv[3] - m_use);
     st.l += (e0 + e1) + (e2 + e3);
+    // Each weight goes to the value product as two bf16 terms: its rounding
+    // and the rounding residual (exact in fp32), so the product sees it to
+    // ~2^-18 relative instead of 2^-9.  With one term, rows dominated by a
+    // few keys with far-apart values carry an error of up to 2^-9 times
+    // that spread, on top of the output's own bf16 rounding.
     const uint32_t p01 = pack_bf16x2(e0, e1);
     const uint32_t p23 = pack_bf16x2(e2, e3);
-    // normalizing by the sum of the rounded weights keeps the output an exact
+    const uint32_t q01 = pack_bf16x2(e0 - bf16_lo(p01), e1 - bf16_hi(p01));
+    const uint32_t q23 = pack_bf16x2(e2 - bf16_lo(p23), e3 - bf16_hi(p23));
+    // normalizing by the sum of the weights as fed keeps the output an exact
     // convex combination of value rows
-    st.lr += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+    st.lr += ((bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23))) +
+             ((bf16_lo(q01) + bf16_hi(q01)) + (bf16_lo(q23) + bf16_hi(q23)));
     const i16x4_t pf = __builtin_bit_cast(i16x4_t, u32x2_t{p01, p23});
+    const i16x4_t pl = __builtin_bit_cast(i16x4_t, u32x2_t{q01, q23});
 
     // O^T[16d + 4g + i][row r16] += V^T[16 dims][16 keys] . P^T[16 keys][16 rows]
     // transposed read: lane 16g + 4e + c points at value row 4g + e, dims
@@ -140,6 +149,7 @@ __device__ __forceinline__ void process_chunk(const ChunkRegs &k, const lds_shor
         const i16x4_t vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (i16x4_t __attribute__((address_space(3))) *)(vt + 16 * d));
         o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pl, o[d], 0, 0, 0);
     }
 }
 

@@ -208,6 +208,15 @@ def test_forced_part_counts_several_row_tiles(s_q, h_q, num_parts):
     assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
 
 
+def test_largest_batch():
+    """8192 sequences (the largest batch the scheduler takes) of 0..80
+    tokens at 16 heads: every part walks ~32 sequence segments, most
+    sequences are split, and the merge grid is 8192 sequences tall."""
+    lens = np.random.default_rng(88).integers(0, 81, 8192)
+    x = gen.make_decode(list(lens), s_q=1, h_q=16, causal=False, seed=88)
+    _check(x, what="batch 8192")
+
+
 @pytest.mark.parametrize("num_parts", [None, 3, 40])
 def test_largest_row_count(num_parts):
     """The largest query shape the interface takes: s_q 16 x h_q 128 = 2048
