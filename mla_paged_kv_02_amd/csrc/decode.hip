@@ -126,9 +126,10 @@ __device__ __forceinline__ void process_chunk(const ChunkRegs &k, const lds_shor
     st.l += (e0 + e1) + (e2 + e3);
     // Each weight goes to the value product as two bf16 terms: its rounding
     // and the rounding residual (exact in fp32), so the product sees it to
-    // ~2^-18 relative instead of 2^-9.  With one term, rows dominated by a
-    // few keys with far-apart values carry an error of up to 2^-9 times
-    // that spread, on top of the output's own bf16 rounding.
+    // ~2^-16 relative instead of 2^-8 (bf16 keeps 8 significant bits).
+    // With one term, rows dominated by a few keys with far-apart values
+    // carry an error of up to 2^-8 times that spread, on top of the
+    // output's own bf16 rounding.
     const uint32_t p01 = pack_bf16x2(e0, e1);
     const uint32_t p23 = pack_bf16x2(e2, e3);
     const uint32_t q01 = pack_bf16x2(e0 - bf16_lo(p01), e1 - bf16_hi(p01));
