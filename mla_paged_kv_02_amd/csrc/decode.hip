@@ -72,8 +72,8 @@ __device__ __forceinline__ void load_chunk(ChunkRegs &k, const DecodeParams &p,
 struct RowState {
     float m;        // running max (log2 units) used as the exponent origin
     float l;        // this lane's share of sum_j 2^(s_j - m), fp32 (gives the lse)
-    float lr;       // the same sum over the bf16-rounded weights fed to the
-                    // value product (normalizes the output)
+    float lr;       // the same sum over the weights as fed to the value
+                    // product, both bf16 terms (normalizes the output)
 };
 
 __device__ __forceinline__ void process_chunk(const ChunkRegs &k, const lds_short_t *qs,

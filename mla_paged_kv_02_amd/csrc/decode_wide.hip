@@ -35,8 +35,10 @@
 //    of tile t with the DMA of tile t + 2 threaded through it, then the
 //    softmax of tile t interleaved with the value product of tile t - 1, so
 //    the matrix pipe has independent work while the wave does vector math.
-//  * Online softmax in fp32, log2 domain, with exact and bf16-rounded sums as
-//    in decode.hip.  O is never rescaled inside the tile loop (it lives in
+//  * Online softmax in fp32, log2 domain, with an exact sum (lse) and one
+//    over the weights as fed, each weight rounded to one bf16 term (the
+//    16-row kernel feeds two; here a second term would double the value
+//    MFMAs).  O is never rescaled inside the tile loop (it lives in
 //    the 256 accumulator registers, and any VALU rescale would force copies
 //    of all of them through VGPRs): a row's first visible key sets its
 //    exponent origin, and if a later score exceeds the origin by more than
