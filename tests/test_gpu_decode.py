@@ -363,6 +363,33 @@ def test_metadata_at_the_largest_batch_and_lengths():
     assert m[8 * parts + 8192 + 1] == 8192 * ((1 << 21) // 16)   # total chunks
 
 
+@pytest.mark.parametrize("batch,num_parts,s_q,h_q", [
+    (1, 1, 1, 16), (3, 256, 1, 16), (64, 1, 2, 64), (64, 256, 1, 16), (256, 256, 1, 16),
+    (256, 256, 1, 128), (257, 256, 1, 16), (256, 257, 2, 128), (200, 37, 1, 32)])
+def test_schedule_batch_and_part_counts(batch, num_parts, s_q, h_q):
+    """mla_get_metadata at batch and part counts from 1 to 257 (one to
+    several sequences and parts per scheduler thread, more parts than
+    sequences and the reverse), with empty sequences among random lengths
+    and with every sequence empty, matches the independent derivation bit
+    for bit."""
+    rng = np.random.default_rng(batch * 1000 + num_parts)
+    lens = rng.integers(0, 3000, batch).astype(np.int32)
+    lens[rng.random(batch) < 0.2] = 0
+    lead = sc.lead_for(s_q, h_q)
+    for seqlens in (lens, np.zeros(batch, dtype=np.int32)):
+        meta, parts = mla.get_metadata(torch.from_numpy(seqlens).cuda(), s_q, h_q, num_parts)
+        torch.cuda.synchronize()
+        assert np.array_equal(meta.cpu().numpy(), sc.expected_metadata(seqlens, parts, lead))
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_all_sequences_empty(h_q):
+    """A batch in which every sequence is empty: no part gets work, every row
+    is out = 0 and lse = -inf."""
+    x = gen.make_decode([0, 0, 0, 0, 0], s_q=1, h_q=h_q, causal=False, seed=91)
+    _check(x, what="all empty h_q=%d" % h_q)
+
+
 def test_debug_checks_reject_out_of_range_tables(monkeypatch):
     """MLA_DEBUG_CHECKS=1: valid inputs (with -1 in the unused columns) give
     the usual result; a used entry outside the cache or a length past the
