@@ -79,7 +79,8 @@ EDGE_LENGTHS = [1, 15, 16, 17, 63, 64, 65, 0, 2, 200, 129, 31]
 
 @pytest.mark.parametrize("s_q,h_q,causal", [(1, 16, False), (2, 16, True), (1, 32, False),
                                             (4, 16, True), (1, 64, False), (3, 32, True),
-                                            (1, 128, False), (2, 64, False), (16, 16, True)])
+                                            (1, 128, False), (2, 64, False), (16, 16, True),
+                                            (2, 16, False), (1, 16, True), (1, 128, True)])
 def test_edge_lengths(s_q, h_q, causal):
     x = gen.make_decode(EDGE_LENGTHS, s_q=s_q, h_q=h_q, causal=causal, seed=100 + s_q * h_q)
     _check(x, what="edge s_q=%d h_q=%d causal=%d" % (s_q, h_q, causal))
