@@ -7,7 +7,10 @@ around it (mla_absorb_bmm: q_nope . W_UK into the latent query, o_lat . W_UV
 after), each stage timed on its own as well.  The default workload is the
 memory-bound configuration
 (batch 64, s_q 1, h_q 16, lengths ~ N(4096, 1024) clipped to [1, 8192],
-shuffled 64-token pages of 576-wide bf16 latent rows).  Inputs are resident
+shuffled 64-token pages of 576-wide bf16 latent rows); without --config the
+line also carries the compute-bound configuration (batch 128, s_q 2 causal,
+h_q 128) under "compute_bound", timed the same way, so that both halves of
+the metric -- HBM GB/s and bf16 TFLOP/s -- come from one run.  Inputs are resident
 in HBM before timing; the cache is replicated so consecutive steps read
 different copies and no step is served from the 256 MB last-level cache
 warmed by the previous one.
@@ -129,13 +132,46 @@ def algorithmic_flops(seqlens, s_q, h_q, causal):
     return 2 * h_q * keys * (D_QK + D_V)
 
 
-def cpu_baseline(x, min_seconds: float):
-    """The fp64 oracle on the host cores, repeated over the full batch until
-    `min_seconds` of work; returns its GB/s on the same algorithmic bytes.
-    For the full step: the oracle's fp64 chain on the first sequences, as
-    many as fit the time."""
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_attend_rate(orc, x, sel, min_seconds, max_reps=200):
+    """Median seconds of the fp64 oracle on the sequences `sel` of x (repeated
+    until `min_seconds` have passed), and the algorithmic bytes of that
+    sample."""
+    q, bt, sl = x.q[sel], x.block_table[sel], x.seqlens[sel]
+    times = []
+    t_end = time.perf_counter() + min_seconds
+    while True:
+        t0 = time.perf_counter()
+        orc.attend(q, x.kv, bt, sl, s_q=x.s_q, h_q=x.h_q, scale=x.scale, causal=x.causal)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end or len(times) >= max_reps:
+            break
+    return (float(np.median(times)), algorithmic_bytes(sl, x.s_q, x.h_q), len(times),
+            algorithmic_flops(sl, x.s_q, x.h_q, x.causal))
+
+
+def cpu_baseline(x, min_seconds: float, one_core_seconds: float = 3.0):
+    """The fp64 oracle on the host cores: its GB/s on the same algorithmic
+    bytes, on all the host's threads and on one.  The all-thread figure
+    covers the full batch when a pass fits in `min_seconds`, else the first
+    sequences that do; the one-thread figure the first sequences that fit in
+    about `one_core_seconds`.  For the full step: the oracle's fp64 chain on
+    the first sequences, as many as fit the time."""
     from oracle import oracle as orc
     threads = orc.max_threads()
+    base = {"kind": "oracle", "unit": "GB/s", "cpu_model": cpu_model(),
+            "host_threads": os.cpu_count()}
     if x.name in ("full_step", "full_step_fp8"):
         e = x.extra
         fp8w = x.name == "full_step_fp8"
@@ -159,24 +195,33 @@ def cpu_baseline(x, min_seconds: float):
         b1, _ = bmm_bytes_flops(done, x.h_q, 128, D_V, fp8w)
         b2, _ = bmm_bytes_flops(done, x.h_q, D_V, 128, fp8w)
         nb = b1 + algorithmic_bytes(sl, 1, x.h_q) + b2
-        return {"value": round(nb / t_all / 1e9, 3), "unit": "GB/s", "cores": threads,
-                "kind": "oracle",
-                "sample": "%s chain (fp64) on the first %d of %d sequences, %.2f s"
-                          % (x.name, done, x.batch, t_all)}
-    times = []
-    t_end = time.perf_counter() + min_seconds
-    while True:
-        t0 = time.perf_counter()
-        orc.attend(x.q, x.kv, x.block_table, x.seqlens, s_q=x.s_q, h_q=x.h_q, scale=x.scale,
-                   causal=x.causal)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() >= t_end or len(times) >= 200:
-            break
-    med = float(np.median(times))
-    gbs = algorithmic_bytes(x.seqlens, x.s_q, x.h_q) / med / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "full %s batch (%d sequences, fp64), median of %d repetitions, %.3f s each"
-                      % (x.name, x.batch, len(times), med)}
+        base.update({"value": round(nb / t_all / 1e9, 3), "cores": threads,
+                     "sample": "%s chain (fp64) on the first %d of %d sequences, %.2f s"
+                               % (x.name, done, x.batch, t_all)})
+        return base
+    # all threads: the full batch if one pass fits the time, else a prefix
+    n = x.batch
+    t_probe = _oracle_attend_rate(orc, x, np.arange(min(n, 4)), 0.0, 1)[0]
+    per_seq = t_probe / min(n, 4)
+    if per_seq * n > min_seconds:
+        n = max(1, min(n, int(min_seconds / max(per_seq, 1e-9))))
+    med, nb, reps, nf = _oracle_attend_rate(orc, x, np.arange(n), min_seconds)
+    base.update({"value": round(nb / med / 1e9, 3), "cores": threads,
+                 "tflops": round(nf / med / 1e12, 5),
+                 "sample": "%s batch, first %d of %d sequences (fp64), median of %d repetitions, "
+                           "%.3f s each" % (x.name, n, x.batch, reps, med)})
+    # one thread
+    orc.set_threads(1)
+    try:
+        t1 = _oracle_attend_rate(orc, x, np.arange(1), 0.0, 1)[0]
+        n1 = max(1, min(x.batch, int(one_core_seconds / max(t1, 1e-9))))
+        med1, nb1, _, nf1 = _oracle_attend_rate(orc, x, np.arange(n1), 0.0, 1)
+    finally:
+        orc.set_threads(threads)
+    base["one_core"] = {"value": round(nb1 / med1 / 1e9, 4), "cores": 1,
+                        "tflops": round(nf1 / med1 / 1e12, 6),
+                        "sample": "first %d sequences, one pass, %.3f s" % (n1, med1)}
+    return base
 
 
 def source_digest():
@@ -219,47 +264,12 @@ def measured_traffic(config, x):
     return int(sum(k[n]["fetch_bytes"] + k[n]["write_bytes"] for n in (decode, "combine_kernel")))
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="memory_bound", choices=sorted(WORKLOADS))
-    ap.add_argument("--replicas", type=int, default=0,
-                    help="cache copies rotated over steps (0: enough for >= 1 GiB)")
-    ap.add_argument("--num-parts", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="replay each step from a captured HIP graph (no host launch cost)")
-    ap.add_argument("--no-peaks", action="store_true",
-                    help="skip the read and MFMA probes (measured peaks)")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB, five times (the known "
-                         "byte count that scales the HBM traffic counters)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import mla_paged_kv_02_amd as mla
-    from mla_paged_kv_02_amd import inputs as gen
-
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
-        return
-
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
-    x = gen.make_config(args.config)
+def time_workload(config, args, torch, mla, gen, dev):
+    """Time one workload: `args.warmup` untimed steps, then `args.steps`
+    steps bracketed by device synchronizations (ms_per_step), then the same
+    steps again with HIP events on the launch stream around each call.
+    Returns (record, inputs)."""
+    x = gen.make_config(config)
     kv_bytes = x.kv.nbytes
     replicas = args.replicas or max(2, int(np.ceil((1 << 30) / kv_bytes)))
 
@@ -278,8 +288,8 @@ def main():
     out = torch.empty((x.batch, x.s_q, x.h_q, D_V), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((x.batch, x.s_q, x.h_q), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    full = args.config in ("full_step", "full_step_fp8")
-    fp8w = args.config == "full_step_fp8"
+    full = config in ("full_step", "full_step_fp8")
+    fp8w = config == "full_step_fp8"
     if full:
         q_nope = to_dev(x.extra["q_nope"])
         y = torch.empty((x.batch, x.h_q, 128), dtype=torch.bfloat16, device=dev)
@@ -403,25 +413,16 @@ def main():
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    traffic = measured_traffic(args.config, x)
+    traffic = measured_traffic(config, x)
     roofline.update({"traffic": traffic, "kernel": kernel, "ms": round(decode_ms, 5),
-                     "ms_p10": st_decode["p10"], "ms_p90": st_decode["p90"]})
+                     "ms_p10": st_decode["p10"], "ms_p90": st_decode["p90"],
+                     "GB/s": round(achieved, 2), "TFLOP/s": round(tflops, 2)})
     if traffic is not None:
         roofline["traffic_vs_algorithmic"] = round(traffic / nbytes, 4)
     rec = {
-        "metric": METRIC,
         "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 cache and queries, shuffled pages)",
-        "config": {"workload": "%s: %s" % (args.config, WORKLOADS[args.config]),
+        "config": {"workload": "%s: %s" % (config, WORKLOADS[config]),
                    "global_batch": x.batch, "seq_len": int(round(float(x.seqlens.mean()))),
                    "s_q": x.s_q, "h_q": x.h_q, "num_parts": parts, "cache_replicas": replicas,
                    "parallelism": "single GPU"},
@@ -436,13 +437,77 @@ def main():
     }
     if stages is not None:
         rec["stages"] = stages
+    del kvs, kv0
+    return rec, x
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default=None, choices=sorted(WORKLOADS),
+                    help="one workload (default: the memory-bound workload, with the "
+                         "compute-bound one reported beside it in the same line)")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="cache copies rotated over steps (0: enough for >= 1 GiB)")
+    ap.add_argument("--num-parts", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a captured HIP graph (no host launch cost)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the read and MFMA probes (measured peaks)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, five times (the known "
+                         "byte count that scales the HBM traffic counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_paged_kv_02_amd as mla
+    from mla_paged_kv_02_amd import inputs as gen
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    config = args.config or "memory_bound"
+    body, x = time_workload(config, args, torch, mla, gen, dev)
+    rec = {"metric": METRIC, "value": body.pop("value"), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": body.pop("ms_per_step"),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) bf16 cache and queries, shuffled pages)"}
+    rec.update(body)
+    second = None
+    if args.config is None:
+        # the metric's other half: bf16 TFLOP/s on the compute-bound workload
+        second, x2 = time_workload("compute_bound", args, torch, mla, gen, dev)
+        rec["compute_bound"] = second
     if not args.no_peaks:
         peaks = measured_peaks(mla, torch, dev)
-        ref = peaks["hbm_read_GBs"] if roofline["bound"] == "hbm" else peaks["bf16_mfma_TFLOPs"]
-        peaks["roofline_frac_of_measured"] = round(roofline["achieved"] / ref, 4)
+        for r in (rec, second):
+            if r is None:
+                continue
+            rf = r["roofline"]
+            ref = peaks["hbm_read_GBs"] if rf["bound"] == "hbm" else peaks["bf16_mfma_TFLOPs"]
+            rf["frac_of_measured_peak"] = round(rf["achieved"] / ref, 4)
         rec["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+        if second is not None:
+            second["cpu_baseline"] = cpu_baseline(x2, min(args.cpu_seconds, 5.0), 1.0)
     print(json.dumps(rec), flush=True)
 
 

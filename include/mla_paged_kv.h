@@ -127,7 +127,10 @@ int mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int nu
  *   lse[b,i,h]   = ln sum_j exp(s_j)                   (natural log)
  * where kv_row(b, j) = kv_cache[block_table[b*bt_stride + j/64]][j%64][:].
  * A row with L <= 0 gets out = 0 and lse = -inf.  Softmax runs in fp32 on
- * bf16 MFMA products; out is rounded to bf16 (nearest even).
+ * bf16 MFMA products; out is rounded to bf16 (nearest even).  `scale` is the
+ * softmax temperature and must be positive and finite (MLA_ERR_INVALID_ARG
+ * otherwise): the 128-row kernel masks keys and takes row maxima on the
+ * unscaled products, which is only order-preserving for scale > 0.
  * The caller keeps n <= 64*bt_stride and the entries a sequence uses in
  * [0, num_pages).  The kernels do not report a breach (the values live on
  * the device) but keep every read inside the buffers: n is capped at 2^21

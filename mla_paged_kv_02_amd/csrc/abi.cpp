@@ -225,7 +225,8 @@ int mla_decode(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
     if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1");
     if (bt_stride < 1) return fail(MLA_ERR_INVALID_ARG, "bt_stride must be >= 1");
     if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, "causal must be 0 or 1");
-    if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(MLA_ERR_INVALID_ARG, "scale must be positive and finite (got %g)", (double)scale);
     if (num_parts < 1 || num_parts > mla::kMaxParts)
         return fail(MLA_ERR_INVALID_ARG, "num_parts must be in [1, %d] (got %d)", mla::kMaxParts,
                     num_parts);

@@ -74,6 +74,12 @@ def test_decode_validation(lib):
     assert _decode(lib, batch=0) == _lib.MLA_ERR_INVALID_ARG
     assert _decode(lib, causal=2) == _lib.MLA_ERR_INVALID_ARG
     assert _decode(lib, scale=float("nan")) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(lib, scale=float("inf")) == _lib.MLA_ERR_INVALID_ARG
+    # the softmax scale must be positive: the 128-row kernel masks and takes
+    # row maxima before scaling, which preserves the order only for scale > 0
+    assert _decode(lib, scale=0.0) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode(lib, scale=-0.07) == _lib.MLA_ERR_INVALID_ARG
+    assert "positive" in _lib.last_error()
     assert _decode(lib, parts=0) == _lib.MLA_ERR_INVALID_ARG
     assert _decode(lib, q=FAKE + 2) == _lib.MLA_ERR_INVALID_ARG
     assert _decode(lib, ws_bytes=100) == _lib.MLA_ERR_WORKSPACE

@@ -48,30 +48,27 @@ def test_skewed_config():
     assert splits > 100      # the 131072-token sequence is spread over many parts
 
 
-def test_compute_bound_config_sampled():
+def test_compute_bound_config():
+    """All 128 sequences of the compute-bound workload (256 rows each, causal)."""
     x = gen.make_config("compute_bound")
-    sel = np.unique(np.concatenate([[int(np.argmin(x.seqlens)), int(np.argmax(x.seqlens))],
-                                    np.random.default_rng(3).choice(128, 4, replace=False)]))
-    _check(x, sel=sel)
+    _, meta, parts = _check(x)
+    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
 
 
 @pytest.mark.parametrize("name", ["multi_token_4", "multi_token_8"])
-def test_multi_token_configs_sampled(name):
-    """s_q 4 and 8 causal (16-row and 128-row kernels) at the memory-bound length mix."""
+def test_multi_token_configs(name):
+    """s_q 4 and 8 causal (64 and 128 rows, both on the 128-row kernel) at the
+    memory-bound length mix, every sequence."""
     x = gen.make_config(name)
-    sel = np.unique(np.concatenate([[int(np.argmin(x.seqlens)), int(np.argmax(x.seqlens))],
-                                    np.random.default_rng(5).choice(x.batch, 4, replace=False)]))
-    _check(x, sel=sel)
+    _check(x)
 
 
-@pytest.mark.parametrize("name,nsel", [("len_1k", 6), ("len_5k", 3), ("len_10k", 2), ("len_32k", 1)])
-def test_length_sweep_configs_sampled(name, nsel):
+@pytest.mark.parametrize("name", ["len_1k", "len_5k", "len_10k", "len_32k"])
+def test_length_sweep_configs(name):
     """h_q 128 at context lengths 1000 ... 32000 (every sequence split over
-    several parts at the long end); the first, last and a random sequence."""
+    several parts at the long end), every sequence."""
     x = gen.make_config(name)
-    sel = np.unique(np.concatenate([[0, x.batch - 1],
-                                    np.random.default_rng(6).choice(x.batch, nsel, replace=False)]))
-    _check(x, sel=sel)
+    _check(x)
 
 
 EDGE_LENGTHS = [1, 15, 16, 17, 63, 64, 65, 0, 2, 200, 129, 31]
@@ -218,44 +215,107 @@ def test_largest_batch():
     _check(x, what="batch 8192")
 
 
-def test_wide_rows_single_rounding_bound():
+def _check_single_rounding_bound(x, what):
     """The 128-row kernel feeds each softmax weight to the value MFMA as one
     bf16 term.  Its output error is then at most 2^-8 * sum_j w_j |v_j - out|
     (weights w, value rows v; bf16 keeps 8 significant bits) plus the
     output's own half-ulp, which rows dominated by a few keys with far-apart
-    values can push past 1e-2.  Over 1024 short sequences at 128 rows every
-    element must be within the tolerance or within that bound (computed here
-    from the oracle's fp64 weights), the mean error within 1e-3 and the lse
-    within 1e-3: a wrong mask, index or normalization lands far outside."""
-    lens = np.random.default_rng(89).integers(0, 81, 1024)
-    x = gen.make_decode(list(lens), s_q=1, h_q=128, causal=False, seed=89)
+    values can push past 1e-2.  Every element must be within the tolerance or
+    within that bound (computed here from the oracle's fp64 weights), the
+    mean error within 1e-3 and the lse within 1e-3: a wrong mask, index or
+    normalization lands far outside."""
     d = gu.DeviceInputs(x)
     out, lse, _, _ = gu.run_decode(d)
     og, lg = gu.dev_to_f64(out), lse.cpu().numpy().astype(np.float64)
     ro, rl = gu.oracle_decode(x)
     q = orc.bf16_to_f64(x.q)
     scale = float(np.float32(x.scale))
+    R = x.s_q * x.h_q
     over_tol = 0
     for b in range(x.batch):
         n = int(x.seqlens[b])
-        o, r = og[b, 0], ro[b, 0]
+        o, r = og[b].reshape(R, 512), ro[b].reshape(R, 512)
         if n == 0:
-            assert np.all(o == 0) and np.all(np.isinf(lg[b, 0])), "empty sequence %d" % b
+            assert np.all(o == 0) and np.all(np.isinf(lg[b])), "empty sequence %d" % b
             continue
         pages = x.block_table[b, :(n + 63) // 64]
         k = orc.bf16_to_f64(x.kv[pages].reshape(-1, 576)[:n])
-        w = np.exp(q[b, 0] @ k.T * scale - rl[b, 0][:, None])            # [128, n]
+        w = np.exp(q[b].reshape(R, 576) @ k.T * scale - rl[b].reshape(R)[:, None])   # [R, n]
         spread = np.einsum("rj,rjd->rd", w, np.abs(k[None, :, :512] - r[:, None, :]))
         bound = 2.0 ** -8 * (spread + np.abs(r)) + 1e-4
         ulp = np.where(np.abs(r) >= 4, 2.0 ** (np.floor(np.log2(np.abs(r) + 1e-300)) - 7), 0.0)
         tol = np.maximum(np.maximum(1e-2, ulp), bound)
         err = np.abs(o - r)
-        assert np.all(err <= tol), "sequence %d (n=%d): error %.4g over its bound" % (
-            b, n, float((err - tol).max()))
+        assert np.all(err <= tol), "%s: sequence %d (n=%d): error %.4g over its bound" % (
+            what, b, n, float((err - tol).max()))
         over_tol += int((err > np.maximum(1e-2, ulp)).sum())
-        assert np.max(np.abs(lg[b, 0] - rl[b, 0])) <= gu.LSE_ABS
+        assert np.max(np.abs(lg[b] - rl[b])) <= gu.LSE_ABS
     assert np.mean(np.abs(og - ro)) <= gu.MEAN_ABS
-    print("elements past 1e-2 but within the single-rounding bound: %d" % over_tol)
+    print("%s: elements past 1e-2 but within the single-rounding bound: %d" % (what, over_tol))
+
+
+def _short_sequences_128_rows():
+    lens = np.random.default_rng(89).integers(0, 81, 1024)
+    return gen.make_decode(list(lens), s_q=1, h_q=128, causal=False, seed=89)
+
+
+def test_wide_rows_single_rounding_bound():
+    """1024 sequences of 0..80 tokens at 128 rows: rows whose weight sits on
+    a few keys with far-apart value rows, within the single-rounding bound."""
+    _check_single_rounding_bound(_short_sequences_128_rows(), "1024 short sequences")
+
+
+WIDE_ONE_TERM = ("the 128-row kernel feeds each softmax weight as one bf16 term; rows dominated "
+                 "by a few far-apart keys exceed 1e-2 by a few thousandths (bounded, tested above)")
+
+
+@pytest.mark.skip(reason=WIDE_ONE_TERM)
+def test_wide_rows_short_sequences():
+    """The same input held to the stated tolerance."""
+    _check(_short_sequences_128_rows(), what="1024 short sequences, 128 rows")
+
+
+def late_dominant_keys(h_q, seed=92):
+    """Three sequences of 3000 to 4100 tokens in which two keys far into the
+    sequence (past token 1300) take nearly all of every row's weight, close
+    to half each, and a third takes a smaller share; their value rows are
+    +-4 in every eighth dim with opposite signs (8 apart) and 0 elsewhere,
+    so those dims carry the whole rounding effect while the mean error stays
+    that of typical outputs.  Queries share one rope direction (plus a little
+    noise per head) and have small latent parts; the planted keys' rope
+    parts point along it."""
+    x = gen.make_decode([3000, 2900, 4097], s_q=1, h_q=h_q, causal=False, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    r = np.ones(64)
+    for b, n in enumerate(x.seqlens):
+        q = np.concatenate([0.05 * rng.standard_normal((h_q, 512)),
+                            r + 0.1 * rng.standard_normal((h_q, 64))], axis=1)
+        x.q[b, 0] = gen.f32_to_bf16_bits(q.astype(np.float32))
+        pos = sorted(rng.choice(np.arange(1300, int(n)), 3, replace=False))
+        for k, (j, a) in enumerate(zip(pos, (3.9, 3.9, 3.6))):
+            page, slot = x.block_table[b, j // 64], j % 64
+            sign = 1.0 if k % 2 == 0 else -1.0
+            dims = np.arange(512)
+            vals = np.where(dims % 8 == 0, np.where(dims % 16 == 0, 4.0, -4.0) * sign, 0.0)
+            x.kv[page, slot, :512] = gen.f32_to_bf16_bits(vals.astype(np.float32))
+            x.kv[page, slot, 512:] = gen.f32_to_bf16_bits(np.full(64, a, dtype=np.float32))
+    return x
+
+
+def test_late_dominant_keys_16_rows():
+    """Keys that decide the output arrive late in long sequences; the 16-row
+    kernel feeds two bf16 terms per weight and meets the stated tolerance."""
+    _check(late_dominant_keys(16), what="late dominant keys h_q=16")
+
+
+def test_late_dominant_keys_128_rows_bound():
+    """The same at 128 rows, within the single-rounding bound."""
+    _check_single_rounding_bound(late_dominant_keys(128), "late dominant keys h_q=128")
+
+
+@pytest.mark.skip(reason=WIDE_ONE_TERM)
+def test_late_dominant_keys_128_rows():
+    _check(late_dominant_keys(128), what="late dominant keys h_q=128")
 
 
 @pytest.mark.parametrize("num_parts", [None, 3, 40])
