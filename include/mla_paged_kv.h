@@ -167,6 +167,27 @@ int mla_decode(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
                void *stream);
 
 /*
+ * The same decode for callers that cannot allocate device memory -- code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation: identical arguments and results to mla_decode without the
+ * workspace, whose partial results go instead to a scratch array the
+ * library owns, MLA_NOALLOC_SCRATCH_BYTES (160 MiB) on each device it runs
+ * on, held from the first call on that device until the process ends.
+ * Returns MLA_ERR_WORKSPACE, launching nothing, when
+ * mla_workspace_bytes(batch, s_q, h_q, num_parts) exceeds it (use mla_decode
+ * there).  The call allocates nothing, copies nothing to the host and never
+ * synchronizes (MLA_DEBUG_CHECKS does not apply to it).  Every call on one
+ * device shares that device's array and leaves its contents behind; calls
+ * that overlap in time on one device (other streams, other threads) race.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)160 << 20)
+int mla_decode_noalloc(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
+                       const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens,
+                       int batch, int s_q, int h_q, int d_qk, int d_v, int page_size, float scale,
+                       int causal, int32_t *metadata, int num_parts, uint16_t *out, float *lse,
+                       void *stream);
+
+/*
  * Split-KV merge.  Sequence b's partial results are slots
  * [split_offsets[b], split_offsets[b+1]) of o_part / lse_part; each slot
  * holds a normalized partial output and its natural-log lse over a disjoint

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_page
 # exported symbols, in header order
 SYMBOLS = ("mla_status_str", "mla_last_error", "mla_device_cus", "mla_default_num_parts",
            "mla_metadata_ints", "mla_workspace_bytes", "mla_get_metadata", "mla_decode",
-           "mla_combine", "mla_absorb_bmm", "mla_absorb_bmm_fp8w", "mla_probe_read",
+           "mla_decode_noalloc", "mla_combine", "mla_absorb_bmm", "mla_absorb_bmm_fp8w", "mla_probe_read",
            "mla_probe_mfma")
 
 MLA_OK = 0
@@ -21,6 +21,8 @@ MLA_ERR_INVALID_ARG = 1
 MLA_ERR_UNSUPPORTED = 2
 MLA_ERR_WORKSPACE = 3
 MLA_ERR_HIP = 4
+# bytes of the scratch array mla_decode_noalloc uses on each device
+NOALLOC_SCRATCH_BYTES = 160 << 20
 
 _lib = None
 
@@ -58,6 +60,9 @@ def load() -> ctypes.CDLL:
     lib.mla_decode.restype = i32
     lib.mla_decode.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, i32, i32, i32,
                                ctypes.c_float, i32, P, i32, P, sz, P, P, P]
+    lib.mla_decode_noalloc.restype = i32
+    lib.mla_decode_noalloc.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, i32, i32, i32,
+                                       ctypes.c_float, i32, P, i32, P, P, P]
     lib.mla_combine.restype = i32
     lib.mla_combine.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P]
     lib.mla_absorb_bmm.restype = i32

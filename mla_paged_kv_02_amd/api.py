@@ -128,6 +128,45 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
     return out, lse
 
 
+
+def decode_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                   seqlens: torch.Tensor, metadata: torch.Tensor, num_parts: int, *,
+                   scale: float, causal: bool = False, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode_noalloc: the same decode with the split partials in the
+    library's own per-device scratch array (no workspace argument; with `out`
+    and `lse` given, nothing is allocated on this path either)."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16)
+    _need(kv_cache, "kv_cache", torch.bfloat16, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(seqlens, "seqlens", torch.int32, dev)
+    _need(metadata, "metadata", torch.int32, dev)
+    if q.dim() != 4 or kv_cache.dim() != 3 or block_table.dim() != 2:
+        raise ValueError("q must be 4-D, kv_cache 3-D and block_table 2-D")
+    B, s_q, h_q, d_qk = q.shape
+    num_pages, page, d_kv = kv_cache.shape
+    if d_kv != d_qk:
+        raise ValueError("q and kv_cache widths differ (%d vs %d)" % (d_qk, d_kv))
+    if block_table.shape[0] != B or seqlens.shape[0] != B:
+        raise ValueError("block_table and seqlens must have batch %d rows" % B)
+    if metadata.numel() < metadata_ints(B, num_parts):
+        raise ValueError("metadata was built for another batch or num_parts")
+    if out is None:
+        out = torch.empty((B, s_q, h_q, D_V), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    if tuple(out.shape) != (B, s_q, h_q, D_V) or tuple(lse.shape) != (B, s_q, h_q):
+        raise ValueError("out / lse have the wrong shape")
+    _lib.check(_lib.load().mla_decode_noalloc(
+        q.data_ptr(), kv_cache.data_ptr(), num_pages, block_table.data_ptr(),
+        block_table.stride(0), seqlens.data_ptr(), B, s_q, h_q, d_qk, D_V, page, float(scale),
+        int(bool(causal)), metadata.data_ptr(), num_parts, out.data_ptr(), lse.data_ptr(),
+        _stream(q)), "mla_decode_noalloc")
+    return out, lse
+
 def combine(o_part: torch.Tensor, lse_part: torch.Tensor, split_offsets: torch.Tensor,
             s_q: int, h_q: int, out: Optional[torch.Tensor] = None,
             lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla_paged_kv.so")
 SOURCES = ["abi.cpp", "metadata.hip", "decode.hip", "decode_wide.hip", "combine.hip", "absorb.hip",
-           "probes.hip"]
+           "probes.hip", "noalloc.hip"]
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -136,6 +136,113 @@ int absorb(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h, const uint
 
 }  // namespace
 
+namespace mla {
+
+int set_error(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int decode_call(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
+                const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens, int batch,
+                int s_q, int h_q, int d_qk, int d_v, int page_size, float scale, int causal,
+                int32_t *metadata, int num_parts, const WorkspaceSource &ws, uint16_t *out,
+                float *lse, void *stream)
+{
+    if (!q || !kv_cache || !block_table || !seqlens || !metadata || !out || !lse)
+        return fail(MLA_ERR_INVALID_ARG, "q, kv_cache, block_table, seqlens, metadata, out and "
+                                         "lse must be non-null");
+    if (int st = check_rows(batch, s_q, h_q)) return st;
+    if (batch > mla::kMetaMaxBatch)
+        return fail(MLA_ERR_UNSUPPORTED, "batch must be <= %d (got %d)", mla::kMetaMaxBatch, batch);
+    if (d_qk != 576 || d_v != 512)
+        return fail(MLA_ERR_UNSUPPORTED, "d_qk must be 576 and d_v 512 (got %d, %d)", d_qk, d_v);
+    if (page_size != 64)
+        return fail(MLA_ERR_UNSUPPORTED, "page_size must be 64 (got %d)", page_size);
+    if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1");
+    if (bt_stride < 1) return fail(MLA_ERR_INVALID_ARG, "bt_stride must be >= 1");
+    if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(MLA_ERR_INVALID_ARG, "scale must be positive and finite (got %g)", (double)scale);
+    if (num_parts < 1 || num_parts > mla::kMaxParts)
+        return fail(MLA_ERR_INVALID_ARG, "num_parts must be in [1, %d] (got %d)", mla::kMaxParts,
+                    num_parts);
+    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+        !aligned(block_table, 4) || !aligned(seqlens, 4) || !aligned(metadata, 4))
+        return fail(MLA_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
+    const size_t need = mla_workspace_bytes(batch, s_q, h_q, num_parts);
+    void *workspace = ws.ptr;
+    if (ws.resolve == nullptr) {
+        if (workspace == nullptr || ws.bytes < need || !aligned(workspace, 16))
+            return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu",
+                        need, workspace == nullptr ? (size_t)0 : ws.bytes);
+    } else {
+        if (need > ws.bytes)
+            return fail(MLA_ERR_WORKSPACE,
+                        "this shape needs %zu bytes of workspace, more than the %zu of the "
+                        "library's own scratch buffer; use mla_decode with a workspace",
+                        need, ws.bytes);
+        if (int st = ws.resolve(&workspace)) return st;
+    }
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (ws.debug_checks && debug_checks())
+        if (int bad = check_tables(seqlens, block_table, bt_stride, batch, num_pages, st))
+            return bad;
+
+    const int rows = s_q * h_q;
+    const size_t slots = (size_t)batch + (size_t)num_parts;
+    float *o_part = static_cast<float *>(workspace);
+    float *lse_part = o_part + slots * (size_t)rows * 512;
+
+    mla::DecodeParams p;
+    p.q = q;
+    p.kv = kv_cache;
+    p.block_table = block_table;
+    p.bt_stride = bt_stride;
+    p.page_max = (uint32_t)std::min<int64_t>(num_pages - 1, INT32_MAX);
+    p.seqlens = seqlens;
+    p.meta = metadata;
+    p.num_parts = num_parts;
+    p.s_q = s_q;
+    p.h_q = h_q;
+    p.causal = causal;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.o_part = o_part;
+    p.lse_part = lse_part;
+    p.out = out;
+    p.lse = lse;
+    // 128-row tiles (the last one possibly partly empty) from 48 rows on,
+    // else 16-row tiles
+    const int row_tiles = mla::decode_row_tiles(rows);
+    const hipError_t e = mla::use_wide(rows)
+                             ? mla::launch_decode_wide(p, num_parts, row_tiles, st)
+                             : mla::launch_decode_r16(p, num_parts, row_tiles, st);
+    if (e != hipSuccess) return hip_status(e, "decode kernel launch");
+
+    // the merge may rewrite partials and counters in place (see combine.hip)
+    const mla::MetaLayout L{batch, num_parts};
+    mla::CombineParams c;
+    c.o_part = o_part;
+    c.lse_part = lse_part;
+    c.split_off = metadata + L.split_off();
+    c.extra_off = metadata + L.extra_off();
+    c.heavy_rank = metadata + L.heavy_rank();
+    c.counters = metadata + L.counters();
+    c.rows = rows;
+    c.skip_single = 1;
+    c.out = out;
+    c.lse = lse;
+    return hip_status(mla::launch_combine(c, batch, (int)L.extra_max(), st),
+                      "combine kernel launch");
+}
+
+}  // namespace mla
+
 extern "C" {
 
 const char *mla_status_str(int status)
@@ -212,82 +319,12 @@ int mla_decode(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
                void *workspace, size_t workspace_bytes, uint16_t *out, float *lse,
                void *stream)
 {
-    if (!q || !kv_cache || !block_table || !seqlens || !metadata || !out || !lse)
-        return fail(MLA_ERR_INVALID_ARG, "q, kv_cache, block_table, seqlens, metadata, out and "
-                                         "lse must be non-null");
-    if (int st = check_rows(batch, s_q, h_q)) return st;
-    if (batch > mla::kMetaMaxBatch)
-        return fail(MLA_ERR_UNSUPPORTED, "batch must be <= %d (got %d)", mla::kMetaMaxBatch, batch);
-    if (d_qk != 576 || d_v != 512)
-        return fail(MLA_ERR_UNSUPPORTED, "d_qk must be 576 and d_v 512 (got %d, %d)", d_qk, d_v);
-    if (page_size != 64)
-        return fail(MLA_ERR_UNSUPPORTED, "page_size must be 64 (got %d)", page_size);
-    if (num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1");
-    if (bt_stride < 1) return fail(MLA_ERR_INVALID_ARG, "bt_stride must be >= 1");
-    if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, "causal must be 0 or 1");
-    if (!std::isfinite(scale) || !(scale > 0.f))
-        return fail(MLA_ERR_INVALID_ARG, "scale must be positive and finite (got %g)", (double)scale);
-    if (num_parts < 1 || num_parts > mla::kMaxParts)
-        return fail(MLA_ERR_INVALID_ARG, "num_parts must be in [1, %d] (got %d)", mla::kMaxParts,
-                    num_parts);
-    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
-        !aligned(block_table, 4) || !aligned(seqlens, 4) || !aligned(metadata, 4))
-        return fail(MLA_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
-    const size_t need = mla_workspace_bytes(batch, s_q, h_q, num_parts);
-    if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
-        return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu",
-                    need, workspace == nullptr ? (size_t)0 : workspace_bytes);
-
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (debug_checks())
-        if (int bad = check_tables(seqlens, block_table, bt_stride, batch, num_pages, st))
-            return bad;
-
-    const int rows = s_q * h_q;
-    const size_t slots = (size_t)batch + (size_t)num_parts;
-    float *o_part = static_cast<float *>(workspace);
-    float *lse_part = o_part + slots * (size_t)rows * 512;
-
-    mla::DecodeParams p;
-    p.q = q;
-    p.kv = kv_cache;
-    p.block_table = block_table;
-    p.bt_stride = bt_stride;
-    p.page_max = (uint32_t)std::min<int64_t>(num_pages - 1, INT32_MAX);
-    p.seqlens = seqlens;
-    p.meta = metadata;
-    p.num_parts = num_parts;
-    p.s_q = s_q;
-    p.h_q = h_q;
-    p.causal = causal;
-    p.scale_log2 = scale * 1.4426950408889634f;
-    p.o_part = o_part;
-    p.lse_part = lse_part;
-    p.out = out;
-    p.lse = lse;
-    // 128-row tiles (the last one possibly partly empty) from 48 rows on,
-    // else 16-row tiles
-    const int row_tiles = mla::decode_row_tiles(rows);
-    const hipError_t e = mla::use_wide(rows)
-                             ? mla::launch_decode_wide(p, num_parts, row_tiles, st)
-                             : mla::launch_decode_r16(p, num_parts, row_tiles, st);
-    if (e != hipSuccess) return hip_status(e, "decode kernel launch");
-
-    // the merge may rewrite partials and counters in place (see combine.hip)
-    const mla::MetaLayout L{batch, num_parts};
-    mla::CombineParams c;
-    c.o_part = o_part;
-    c.lse_part = lse_part;
-    c.split_off = metadata + L.split_off();
-    c.extra_off = metadata + L.extra_off();
-    c.heavy_rank = metadata + L.heavy_rank();
-    c.counters = metadata + L.counters();
-    c.rows = rows;
-    c.skip_single = 1;
-    c.out = out;
-    c.lse = lse;
-    return hip_status(mla::launch_combine(c, batch, (int)L.extra_max(), st),
-                      "combine kernel launch");
+    mla::WorkspaceSource ws;
+    ws.ptr = workspace;
+    ws.bytes = workspace_bytes;
+    return mla::decode_call(q, kv_cache, num_pages, block_table, bt_stride, seqlens, batch, s_q,
+                            h_q, d_qk, d_v, page_size, scale, causal, metadata, num_parts, ws,
+                            out, lse, stream);
 }
 
 int mla_combine(const float *o_part, const float *lse_part, const int32_t *split_offsets,

@@ -119,6 +119,25 @@ hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tile
 // `extra_wgs`: upper bound on the extra workgroups of the two-level merge
 hipError_t launch_combine(const CombineParams &p, int batch, int extra_wgs, hipStream_t stream);
 hipError_t launch_absorb(const AbsorbParams &p, int heads, hipStream_t stream);
+// Where mla_decode's partial results go: the caller's workspace (ptr, bytes),
+// or, when `resolve` is set, a buffer of `bytes` that resolve() returns for
+// the current device (the library's own scratch array).
+struct WorkspaceSource {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+    int (*resolve)(void **ptr) = nullptr;
+    bool debug_checks = true;   // honour MLA_DEBUG_CHECKS (host copies and a sync)
+};
+
+// The validated decode call behind mla_decode and mla_decode_noalloc (abi.cpp).
+int decode_call(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
+                const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens, int batch,
+                int s_q, int h_q, int d_qk, int d_v, int page_size, float scale, int causal,
+                int32_t *metadata, int num_parts, const WorkspaceSource &ws, uint16_t *out,
+                float *lse, void *stream);
+// Record a failure reason for mla_last_error(); returns `status`.
+int set_error(int status, const char *fmt, ...);
+
 hipError_t launch_probe_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink,
                              hipStream_t stream);
 hipError_t launch_probe_mfma(int iters, int workgroups, float *sink, hipStream_t stream);

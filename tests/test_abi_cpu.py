@@ -87,6 +87,40 @@ def test_decode_validation(lib):
     assert _decode(lib, ws=None, ws_bytes=1 << 30) == _lib.MLA_ERR_WORKSPACE
 
 
+def _decode_noalloc(lib, **kw):
+    a = dict(q=FAKE, kv=FAKE, num_pages=10, bt=FAKE, bt_stride=4, seqlens=FAKE, batch=2, s_q=1,
+             h_q=16, d_qk=576, d_v=512, page=64, scale=0.07, causal=0, meta=FAKE, parts=4,
+             out=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.mla_decode_noalloc(a["q"], a["kv"], a["num_pages"], a["bt"], a["bt_stride"],
+                                  a["seqlens"], a["batch"], a["s_q"], a["h_q"], a["d_qk"],
+                                  a["d_v"], a["page"], a["scale"], a["causal"], a["meta"],
+                                  a["parts"], a["out"], a["lse"], None)
+
+
+def test_decode_noalloc_validation(lib):
+    """The same argument checks as mla_decode, and a shape whose partials do
+    not fit the library's scratch array is refused before any device call."""
+    assert _decode_noalloc(lib, q=None) == _lib.MLA_ERR_INVALID_ARG
+    assert _decode_noalloc(lib, h_q=8) == _lib.MLA_ERR_UNSUPPORTED
+    assert _decode_noalloc(lib, scale=0.0) == _lib.MLA_ERR_INVALID_ARG
+    # (batch + parts) * rows * 513 * 4 bytes: 8192 sequences at 128 rows do not fit
+    need = lib.mla_workspace_bytes(8192, 1, 128, 256)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert _decode_noalloc(lib, batch=8192, h_q=128, parts=256) == _lib.MLA_ERR_WORKSPACE
+    assert "scratch" in _lib.last_error() and str(need) in _lib.last_error()
+    # the workloads' shapes fit: compute-bound (128 x 256 rows, 128 parts) and
+    # full step (128 x 128 rows, 256 parts)
+    assert lib.mla_workspace_bytes(128, 2, 128, 128) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.mla_workspace_bytes(128, 1, 128, 256) <= _lib.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MLA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+
+
 def test_other_validation(lib):
     assert lib.mla_get_metadata(None, 2, 1, 16, 4, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
     assert lib.mla_get_metadata(FAKE, 20000, 1, 16, 4, FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
