@@ -119,7 +119,10 @@ int mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int nu
                      int32_t *metadata, void *stream);
 
 /*
- * Paged MLA decode.  For every sequence b, query i and head h, with
+ * Paged MLA decode: the MLA decoding kernel of "DeepSeek publica FlashMLA
+ * como codigo abierto" (release bullets: BF16, paged KV cache with 64-token
+ * blocks, variable-length sequences).  For every sequence b, query i and
+ * head h, with
  * n = seqlens[b] and L = n (causal = 0) or L = n - s_q + 1 + i (causal = 1:
  * query i sits at absolute position n - s_q + i):
  *   s_j = scale * <q[b,i,h,:], kv_row(b, j)>         for j < L
@@ -188,7 +191,11 @@ int mla_decode_noalloc(const uint16_t *q, const uint16_t *kv_cache, int64_t num_
                        void *stream);
 
 /*
- * Split-KV merge.  Sequence b's partial results are slots
+ * Split-KV merge of the decode's partial results, the step that lets the
+ * variable-length schedule of "DeepSeek publica FlashMLA como codigo
+ * abierto" (release bullets) cut one sequence's keys over several
+ * workgroups; the merge formula is the log-sum-exp combination of
+ * softmax partials.  Sequence b's partial results are slots
  * [split_offsets[b], split_offsets[b+1]) of o_part / lse_part; each slot
  * holds a normalized partial output and its natural-log lse over a disjoint
  * key range (lse = -inf marks an empty range).  With M = max_s lse_s:
