@@ -48,6 +48,11 @@
  *     W[h,k,n] = bf16( e4m3(code[h,k,n]) * scale[h, k / 128, n / 128] )
  *   where the product is exact and bf16() rounds it once, to nearest even.
  *
+ *   Materialized absorbed weights (the products the same PR description
+ *   decides not to precompute; the fp64 products themselves are formed in
+ *   oracle/materialize.py) are stored as bf16: oracle_round_bf16_array
+ *   rounds each fp64 value once, to nearest even.
+ *
  * Precision: inputs that are bf16 in the product (cache rows, weights) are
  * passed as raw bf16 bit patterns and widened exactly to fp64 here;
  * activations are passed as fp64.  All arithmetic is fp64 and nothing is
@@ -237,6 +242,14 @@ uint16_t oracle_double_to_bf16(double x)
  *   scale [heads][ceil(K / blk)][ceil(N / blk)] fp32
  *   w     [heads][K][N] bf16 bits (output)
  */
+/* x[i] rounded once to bf16 (nearest even), for n values: the storage of
+ * weights that are products of other weights (materialized absorption). */
+void oracle_round_bf16_array(const double *x, int64_t n, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_double_to_bf16(x[i]);
+}
+
 void oracle_dequant_fp8(const uint8_t *code, const float *scale, int heads, int K, int N,
                         int blk, uint16_t *w)
 {

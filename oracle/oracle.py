@@ -50,6 +50,8 @@ def bind(lib):
     lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.oracle_double_to_bf16.restype = ctypes.c_uint16
     lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_round_bf16_array.restype = None
+    lib.oracle_round_bf16_array.argtypes = [P, i64, P]
     lib.oracle_dequant_fp8.restype = None
     lib.oracle_dequant_fp8.argtypes = [P, P, i32, i32, i32, i32, P]
     lib.oracle_set_threads.argtypes = [i32]
@@ -162,6 +164,14 @@ def e4m3_to_f64(code: int) -> float:
 def f64_to_bf16(x: float) -> int:
     """Bit pattern of the bf16 nearest to x (ties to even)."""
     return int(_load().oracle_double_to_bf16(float(x)))
+
+
+def round_bf16(x) -> np.ndarray:
+    """Bit patterns of x (fp64) rounded once to bf16, nearest even."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.zeros(a.shape, dtype=np.uint16)
+    _load().oracle_round_bf16_array(_ptr(a), a.size, _ptr(out))
+    return out
 
 
 def dequant_fp8(codes, scales, blk: int = FP8_BLOCK):
