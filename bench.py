@@ -441,6 +441,84 @@ def time_workload(config, args, torch, mla, gen, dev):
     return rec, x
 
 
+def absorb_ab(args, torch, mla, gen, dev):
+    """Materialized vs sequential absorption at batch 128, 128 heads: HIP-event
+    medians of the query side (c_q -> q_lat) and the output side (o_lat -> y)
+    each way, with a 512 MiB write between timed calls so that no weight is
+    served from the last-level cache, and the weight bytes and flops each
+    way touches (every weight read once per call)."""
+    from mla_paged_kv_02_amd import absorption as ab
+    shp = gen.ABSORB_AB_SHAPE
+    B, H, r, dn, c, dv, dm = (shp[k] for k in ("B", "H", "r", "dn", "c", "dv", "d_model"))
+    t = gen.make_absorb_ab(**shp)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    d = {k: to_dev(v) for k, v in t.items()}
+    del t
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    q = torch.empty((B, 1, H, 576), dtype=torch.bfloat16, device=dev)
+    q_lat = q[:, 0, :, :c]
+    q_nope = torch.empty((B, H, dn), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((B, dm), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn, reps):
+        ts = []
+        for i in range(reps + 3):
+            flush.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            if i >= 3:
+                ts.append(a.elapsed_time(b) * 1e3)
+        return round(float(np.median(ts)), 2)
+
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    w_q_uk, w_uv_o = ab.materialize(d["w_uq"], d["w_uk"], d["w_uv"], d["w_o"])
+    a1.record(stream)
+    a1.synchronize()
+    reps = max(5, min(args.steps, 30))
+    res = {
+        "sequential": {
+            "query_us": timed(lambda: ab.query_sequential(d["c_q"], d["w_uq"], d["w_uk"], q_lat,
+                                                          q_nope), reps),
+            "output_us": timed(lambda: ab.output_sequential(d["o_lat"], d["w_uv"], d["w_o"], y,
+                                                            v), reps)},
+        "materialized": {
+            "query_us": timed(lambda: ab.query_materialized(d["c_q"], w_q_uk, q_lat), reps),
+            "output_us": timed(lambda: ab.output_materialized(d["o_lat"], w_uv_o, y), reps)},
+    }
+    act = 2  # bf16 bytes
+    wq = {"sequential": H * r * dn + H * dn * c, "materialized": H * r * c}
+    wo = {"sequential": H * c * dv + H * dv * dm, "materialized": H * c * dm}
+    for way, rec in res.items():
+        qb = wq[way] * act + (B * r + B * H * c) * act + (B * H * dn * 2 * act if way == "sequential" else 0)
+        ob = wo[way] * act + (B * H * c + B * dm) * act + (B * H * dv * 2 * act if way == "sequential" else 0)
+        rec.update({"query_weight_bytes": wq[way] * act, "output_weight_bytes": wo[way] * act,
+                    "query_flops": 2 * B * wq[way], "output_flops": 2 * B * wo[way],
+                    "query_GBs": round(qb / (rec["query_us"] * 1e-6) / 1e9, 1),
+                    "output_GBs": round(ob / (rec["output_us"] * 1e-6) / 1e9, 1),
+                    "total_us": round(rec["query_us"] + rec["output_us"], 2)})
+    out = {"metric": "materialized vs sequential MLA absorption: weight bytes, flops and time "
+                     "of the query and output projections",
+           "config": {"batch": B, "heads": H, "q_lora_rank": r, "qk_nope": dn, "latent": c,
+                      "v_head": dv, "d_model": dm,
+                      "note": "q_lora_rank and d_model are DeepSeek-V3/R1 values, not on the pages"},
+           "materialize_us": round(a0.elapsed_time(a1) * 1e3, 1),
+           "kernel": "absorb_kernel (mla_absorb_bmm) for every product, HIP events",
+           **res,
+           "weight_bytes_ratio": round((wq["materialized"] + wo["materialized"]) /
+                                       (wq["sequential"] + wo["sequential"]), 3),
+           "time_ratio": round(res["materialized"]["total_us"] / res["sequential"]["total_us"], 3)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -458,6 +536,9 @@ def main():
                     help="replay each step from a captured HIP graph (no host launch cost)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the read and MFMA probes (measured peaks)")
+    ap.add_argument("--absorb-ab", action="store_true",
+                    help="only compare the materialized and sequential absorption projections "
+                         "(one JSON line)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, five times (the known "
                          "byte count that scales the HBM traffic counters)")
@@ -483,6 +564,9 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.absorb_ab:
+        absorb_ab(args, torch, mla, gen, dev)
+        return
     config = args.config or "memory_bound"
     body, x = time_workload(config, args, torch, mla, gen, dev)
     rec = {"metric": METRIC, "value": body.pop("value"), "unit": "GB/s", "n_gpus": 1,

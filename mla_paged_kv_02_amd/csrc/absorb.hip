@@ -19,13 +19,17 @@
 // turn, and each XCD has its own L2: the grid is numbered so that all tiles
 // of a head share an XCD (number L -> XCD L % 8, head L % 8 + 8 ((L / 8) /
 // tiles per head)), which keeps a head's x rows and W slabs in one L2
-// instead of fetching them from HBM once per XCD.
+// instead of fetching them from HBM once per XCD.  With fewer than 8 heads
+// (one head with the heads folded into K is a plain matmul) the tiles are
+// numbered in order instead, so that all XCDs share the work.
 //
 // The same PR stores the weights in fp8 and decompresses them to 16-bit
 // floats for the bmm.  With fp8 weights (OCP E4M3 codes, one fp32 scale per
 // 128 x 128 block) each thread loads 8 codes per slab instead of 8 bf16
 // (half the weight bytes) and decompresses them in registers before the LDS
 // stage; the rest of the kernel is the bf16 one.
+#include <algorithm>
+
 #include "mla_device.h"
 #include "kernels.h"
 
@@ -61,69 +65,124 @@ __device__ __forceinline__ uint32_t round_scaled_bf16x2(float v0, float v1, floa
     }
     return r;
 }
-template <int G, bool kFp8>
-__global__ __launch_bounds__(kAbsThreads) void absorb_kernel(AbsorbParams p)
+// One (head, 64 x 64 output tile) work item: item number idx -> head and
+// tile.  With 8 heads or more, item idx lands on head (idx % 8) + 8 ((idx /
+// 8) / tiles): a persistent grid whose size is a multiple of 8 keeps item
+// idx on the XCD of workgroup idx % 8, so all tiles of a head share one L2.
+// With fewer heads (one head with the heads folded into K is a plain matmul)
+// items are numbered in order, so that every XCD gets work.
+struct AbsItem {
+    int h, n0, m0;
+};
+
+__device__ __forceinline__ AbsItem abs_item(const AbsorbParams &p, int idx, int tiles, int ntn)
 {
-    __shared__ __attribute__((aligned(16))) short wt[G * kAbsKSlab * kWStride];
+    int h, t;
+    if (p.heads >= 8) {
+        const int k8 = idx >> 3;
+        h = (idx & 7) + 8 * (k8 / tiles);
+        t = k8 % tiles;
+    } else {
+        h = idx / tiles;
+        t = idx % tiles;
+    }
+    return AbsItem{h, (t % ntn) * kAbsBN, (t / ntn) * kAbsBM};
+}
+
+// The registers one step loads: G 32-row slabs of W's 64-column slab (bf16,
+// or fp8 codes and their block scale) and of this lane's x row.
+template <int G>
+struct AbsRegs {
+    u32x4_t wv[G], xv[G];
+    u32x2_t wq[G];
+    float wsc[G];
+};
+
+// A workgroup walks its items (idx = blockIdx.x, + gridDim.x, ...) and, in
+// each, the groups of G slabs along K.  Every step issues the next step's
+// global loads before it stages and multiplies the current one, so one
+// step's loads are always in flight behind the matrix work; W's slab goes
+// through one of two LDS buffers (one barrier per step: a buffer is written
+// again only two steps later, after every wave has passed the barrier that
+// follows its last reads).
+template <int G, bool kFp8>
+__global__ __launch_bounds__(kAbsThreads, 2) void absorb_kernel(AbsorbParams p, int total_items)
+{
+    __shared__ __attribute__((aligned(16))) short wt[2][G * kAbsKSlab * kWStride];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int r16 = lane & 15;
     const int g = lane >> 4;
     const int ntn = p.N / kAbsBN;
     const int tiles = ntn * ((p.batch + kAbsBM - 1) / kAbsBM);   // per head
-    const int k8 = blockIdx.x >> 3;
-    const int h = (blockIdx.x & 7) + 8 * (k8 / tiles);
-    if (h >= p.heads) return;   // padding of the head count to a multiple of 8 (uniform)
-    const int t = k8 % tiles;
-    const int n0 = (t % ntn) * kAbsBN;
-    const int m0 = (t / ntn) * kAbsBM;
-
-    const uint16_t *wh = p.w + (int64_t)h * p.K * p.N;
-    const uint8_t *w8h = p.w8 + (int64_t)h * p.K * p.N;
+    const int ngroups = (p.K + G * kAbsKSlab - 1) / (G * kAbsKSlab);
     const int kblocks = (p.K + kFp8Block - 1) / kFp8Block;
     const int nblocks = (p.N + kFp8Block - 1) / kFp8Block;
-    // a 64-column tile lies inside one 128-column scale block
-    const float *sch = p.wscale + ((int64_t)h * kblocks) * nblocks + n0 / kFp8Block;
-    const int brow = m0 + wave * 16 + r16;               // batch row of this lane (B operand)
-    const bool row_ok = brow < p.batch;
-    const uint16_t *xrow = p.x + (int64_t)(row_ok ? brow : 0) * p.x_sb + (int64_t)h * p.x_sh;
-
     // staging: thread t copies 16 bytes of each slab: row t / 8, columns 8 * (t % 8)
     const int srow = threadIdx.x >> 3;
     const int scol = 8 * (threadIdx.x & 7);
-
-    f32x4_t acc[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
     // transposed-read address: lane 16g + 4e + c -> slab row 8g + e, column 4c
     const int tr_row = 8 * g + (r16 >> 2);
     const int tr_col = 4 * (r16 & 3);
 
-    for (int kg = 0; kg < p.K; kg += G * kAbsKSlab) {
+    // the next item of this workgroup at or after idx (padding heads skipped)
+    auto next_item = [&](int idx) {
+        while (idx < total_items && abs_item(p, idx, tiles, ntn).h >= p.heads) idx += gridDim.x;
+        return idx;
+    };
+    // Every step issues the same number of global loads, without branches
+    // and without touching their results (slabs past K re-read the group's
+    // last slab and are not used; rows past the batch read row 0, which only
+    // feeds output rows that are never stored), so the wait before a step's
+    // staging can leave the next step's loads in flight.
+    auto load = [&](AbsRegs<G> &r, const AbsItem &it, int grp) {
+        const int kg = grp * G * kAbsKSlab;
         const int ns = min(G, (p.K - kg) / kAbsKSlab);   // slabs in this group (uniform)
-        u32x4_t wv[G], xv[G];
-        u32x2_t wq[G];      // fp8: 8 codes per thread and slab
-        float wsc[G];       // fp8: the slab's scale (a 32-row slab lies in one block)
+        const int brow = it.m0 + wave * 16 + r16;
+        const uint16_t *xrow =
+            p.x + (int64_t)(brow < p.batch ? brow : 0) * p.x_sb + (int64_t)it.h * p.x_sh;
+        const uint16_t *wh = p.w + (int64_t)it.h * p.K * p.N;
+        const uint8_t *w8h = p.w8 + (int64_t)it.h * p.K * p.N;
+        // a 64-column tile lies inside one 128-column scale block
+        const float *sch = p.wscale + ((int64_t)it.h * kblocks) * nblocks + it.n0 / kFp8Block;
 #pragma unroll
         for (int s = 0; s < G; ++s) {
-            wv[s] = u32x4_t{0u, 0u, 0u, 0u};
-            xv[s] = u32x4_t{0u, 0u, 0u, 0u};
-            wq[s] = u32x2_t{0u, 0u};
-            wsc[s] = 0.f;
-            if (s < ns) {
-                const int k0 = kg + s * kAbsKSlab;
-                if (kFp8) {
-                    wq[s] = *reinterpret_cast<const u32x2_t *>(w8h + (int64_t)(k0 + srow) * p.N +
-                                                               n0 + scol);
-                    wsc[s] = sch[(k0 / kFp8Block) * nblocks];
-                } else {
-                    wv[s] = *reinterpret_cast<const u32x4_t *>(wh + (int64_t)(k0 + srow) * p.N +
-                                                               n0 + scol);
-                }
-                if (row_ok) xv[s] = *reinterpret_cast<const u32x4_t *>(xrow + k0 + 8 * g);
+            const int k0 = kg + min(s, ns - 1) * kAbsKSlab;
+            if (kFp8) {
+                r.wq[s] = *reinterpret_cast<const u32x2_t *>(w8h + (int64_t)(k0 + srow) * p.N +
+                                                             it.n0 + scol);
+                r.wsc[s] = sch[(k0 / kFp8Block) * nblocks];
+            } else {
+                r.wv[s] = *reinterpret_cast<const u32x4_t *>(wh + (int64_t)(k0 + srow) * p.N +
+                                                             it.n0 + scol);
             }
+            r.xv[s] = *reinterpret_cast<const u32x4_t *>(xrow + k0 + 8 * g);
         }
+    };
+
+    int idx = next_item(blockIdx.x);
+    if (idx >= total_items) return;   // uniform
+    AbsItem cur = abs_item(p, idx, tiles, ntn);
+    int grp = 0, buf = 0;
+    f32x4_t acc[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // one step: prefetch the next step into `nx`, then stage and multiply `cr`;
+    // false when this was the workgroup's last step
+    auto step = [&](AbsRegs<G> &cr, AbsRegs<G> &nx) {
+        int nidx = idx, ngrp = grp + 1;
+        if (ngrp == ngroups) {
+            ngrp = 0;
+            nidx = next_item(idx + gridDim.x);
+        }
+        const bool more = nidx < total_items;
+        const AbsItem nit = more ? abs_item(p, nidx, tiles, ntn) : cur;
+        // the last step re-reads its own group (unused), keeping the load count fixed
+        load(nx, nit, more ? ngrp : grp);
+        __builtin_amdgcn_sched_barrier(0);   // the next loads go out before this step's work
+
+        const int ns = min(G, (p.K - grp * G * kAbsKSlab) / kAbsKSlab);
         if (kFp8) {
             // decompress to bf16 in registers, in the layout of the bf16 path
             // (byte i of a word is code i; the pair form decodes bytes 0-1 or 2-3)
@@ -131,66 +190,101 @@ __global__ __launch_bounds__(kAbsThreads) void absorb_kernel(AbsorbParams p)
             for (int s = 0; s < G; ++s)
 #pragma unroll
                 for (int jw = 0; jw < 2; ++jw) {
-                    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wq[s][jw], false);
-                    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wq[s][jw], true);
-                    wv[s][2 * jw] = round_scaled_bf16x2(lo[0], lo[1], wsc[s]);
-                    wv[s][2 * jw + 1] = round_scaled_bf16x2(hi[0], hi[1], wsc[s]);
+                    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cr.wq[s][jw], false);
+                    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cr.wq[s][jw], true);
+                    cr.wv[s][2 * jw] = round_scaled_bf16x2(lo[0], lo[1], cr.wsc[s]);
+                    cr.wv[s][2 * jw + 1] = round_scaled_bf16x2(hi[0], hi[1], cr.wsc[s]);
                 }
         }
-        __syncthreads();   // the previous group fully consumed
+        short *wb = wt[buf];
 #pragma unroll
         for (int s = 0; s < G; ++s)
             if (s < ns)
-                *reinterpret_cast<u32x4_t *>(wt + (s * kAbsKSlab + srow) * kWStride + scol) = wv[s];
+                *reinterpret_cast<u32x4_t *>(wb + (s * kAbsKSlab + srow) * kWStride + scol) =
+                    cr.wv[s];
         __syncthreads();
 #pragma unroll
         for (int s = 0; s < G; ++s) {
             if (s < ns) {
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb) {
-                    const short *base = wt + (s * kAbsKSlab + tr_row) * kWStride + 16 * mb + tr_col;
+                    const short *base = wb + (s * kAbsKSlab + tr_row) * kWStride + 16 * mb + tr_col;
                     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (i16x4_t __attribute__((address_space(3))) *)(base));
                     const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (i16x4_t __attribute__((address_space(3))) *)(base + 4 * kWStride));
                     const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, xv[s]),
+                        __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, cr.xv[s]),
                         acc[mb], 0, 0, 0);
                 }
             }
         }
-    }
-
-    if (!row_ok) return;
-    uint16_t *yrow = p.y + (int64_t)brow * p.y_sb + (int64_t)h * p.y_sh + n0;
+        if (grp == ngroups - 1) {
+            // the item is complete: its 64 x 64 tile goes out, 8 bytes per lane and block
+            const int brow = cur.m0 + wave * 16 + r16;
+            if (brow < p.batch) {
+                uint16_t *yrow = p.y + (int64_t)brow * p.y_sb + (int64_t)cur.h * p.y_sh + cur.n0;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        u32x2_t v;
-        v[0] = pack_bf16x2(acc[mb][0], acc[mb][1]);
-        v[1] = pack_bf16x2(acc[mb][2], acc[mb][3]);
-        *reinterpret_cast<u32x2_t *>(yrow + 16 * mb + 4 * g) = v;
+                for (int mb = 0; mb < 4; ++mb) {
+                    u32x2_t v;
+                    v[0] = pack_bf16x2(acc[mb][0], acc[mb][1]);
+                    v[1] = pack_bf16x2(acc[mb][2], acc[mb][3]);
+                    *reinterpret_cast<u32x2_t *>(yrow + 16 * mb + 4 * g) = v;
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        idx = nidx;
+        grp = ngrp;
+        cur = nit;
+        buf ^= 1;
+        return more;
+    };
+
+    AbsRegs<G> ra, rb;
+    load(ra, cur, 0);
+    // two steps per trip, so the register sets alternate without copies
+    while (step(ra, rb) && step(rb, ra)) {
     }
 }
 
-template <int G>
-void launch_group(const AbsorbParams &p, dim3 grid, hipStream_t stream)
+int absorb_grid_cap()
 {
+    // two workgroups per CU of the current device (cached per device)
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            cus = 256;
+        cached[dev] = 2 * cus;
+    }
+    return cached[dev];
+}
+
+template <int G>
+void launch_group(const AbsorbParams &p, int total_items, hipStream_t stream)
+{
+    int grid = std::min(total_items, absorb_grid_cap());
+    if (grid >= 8) grid -= grid % 8;   // keeps each item on the XCD of workgroup idx % 8
     if (p.w8 != nullptr)
-        hipLaunchKernelGGL((absorb_kernel<G, true>), grid, dim3(kAbsThreads), 0, stream, p);
+        hipLaunchKernelGGL((absorb_kernel<G, true>), dim3(grid), dim3(kAbsThreads), 0, stream, p,
+                           total_items);
     else
-        hipLaunchKernelGGL((absorb_kernel<G, false>), grid, dim3(kAbsThreads), 0, stream, p);
+        hipLaunchKernelGGL((absorb_kernel<G, false>), dim3(grid), dim3(kAbsThreads), 0, stream, p,
+                           total_items);
 }
 
 hipError_t launch_absorb(const AbsorbParams &p, int heads, hipStream_t stream)
 {
     const int tiles = (p.N / kAbsBN) * ((p.batch + kAbsBM - 1) / kAbsBM);
-    const dim3 grid((unsigned)((heads + 7) / 8 * 8) * (unsigned)tiles);
-    // fp8 at K = 512: two groups of 8 slabs (the decompression of one group
-    // overlaps the other's loads; measured faster than one group of 16)
-    if (p.K == 4 * kAbsKSlab) launch_group<4>(p, grid, stream);
-    else if (p.K == 16 * kAbsKSlab && p.w8 == nullptr) launch_group<16>(p, grid, stream);
-    else launch_group<8>(p, grid, stream);
+    const int total = (heads >= 8 ? (heads + 7) / 8 * 8 : heads) * tiles;
+    if (p.K == 4 * kAbsKSlab) launch_group<4>(p, total, stream);
+    else launch_group<8>(p, total, stream);
     return hipGetLastError();
 }
 

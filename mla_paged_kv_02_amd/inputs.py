@@ -238,3 +238,25 @@ def make_config(name: str, seed: Optional[int] = None) -> DecodeInputs:
     return DecodeInputs(q=q, kv=kv, block_table=bt, seqlens=seqlens, s_q=s_q, h_q=h_q,
                         causal=causal, name=name)
 
+
+
+# The materialized-vs-sequential absorption comparison: the pages give 128
+# heads, a 512-wide latent and 128-wide per-head nope query and value; the
+# compressed-query rank (1536) and the model width (7168) are not on them
+# and are taken from DeepSeek-V3 / R1, the model the pages serve.
+ABSORB_AB_SHAPE = dict(B=128, H=128, r=1536, dn=128, c=512, dv=128, d_model=7168)
+
+
+def make_absorb_ab(B=128, H=128, r=1536, dn=128, c=512, dv=128, d_model=7168,
+                   seed: int = 1100) -> dict:
+    """bf16 bits of the compressed query c_q [B, r] (N(0, 1)), the weights
+    W_UQ [H, r, dn], W_UK [H, dn, c], W_UV [H, c, dv], W_O [H, dv, d_model]
+    (N(0, 0.02)) and a latent attention output o_lat [B, H, c] (N(0, 0.25)),
+    each from its own stream of SeedSequence(seed)."""
+    ss = np.random.SeedSequence(seed).spawn(6)
+    g = [np.random.default_rng(s) for s in ss]
+    return dict(c_q=normal_bf16(g[0], (B, r)), w_uq=normal_bf16(g[1], (H, r, dn), std=0.02),
+                w_uk=normal_bf16(g[2], (H, dn, c), std=0.02),
+                w_uv=normal_bf16(g[3], (H, c, dv), std=0.02),
+                w_o=normal_bf16(g[4], (H, dv, d_model), std=0.02),
+                o_lat=normal_bf16(g[5], (B, H, c), std=0.25))
