@@ -36,9 +36,12 @@
 //    softmax of tile t interleaved with the value product of tile t - 1, so
 //    the matrix pipe has independent work while the wave does vector math.
 //  * Online softmax in fp32, log2 domain, with an exact sum (lse) and one
-//    over the weights as fed, each weight rounded to one bf16 term (the
-//    16-row kernel feeds two; here a second term would double the value
-//    MFMAs).  O is never rescaled inside the tile loop (it lives in
+//    over the weights as fed.  Each weight goes to the value product as two
+//    bf16 terms, its rounding and the rounding residual (exact in fp32), on
+//    two MFMAs over the same V^T fragment, so the product sees it to about
+//    2^-16 relative; one term (2^-8) lets rows whose weight sits on a few
+//    keys with far-apart value rows miss 1e-2.  The second term doubles the
+//    value MFMAs (68 -> 100 per wave and tile).  O is never rescaled inside the tile loop (it lives in
 //    the 256 accumulator registers, and any VALU rescale would force copies
 //    of all of them through VGPRs): a row's first visible key sets its
 //    exponent origin, and if a later score exceeds the origin by more than
@@ -460,11 +463,12 @@ __device__ __forceinline__ void pv_read(const int vb[2][2], int d, int kk, i16x4
         (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[1][d & 1] + off));
 }
 
-// O^T[512 dims][32 rows] += V^T P^T for one tile: 32 MFMAs, V^T fragments of
-// (dim block d, k-step kk) at vb[read][d % 2] + 2048 kk + 4096 (d / 2) (keys
-// 16 apart are two row groups apart with the same swizzle)
+// O^T[512 dims][32 rows] += V^T P^T for one tile, each weight as two terms
+// (pf + rf): 64 MFMAs, V^T fragments of (dim block d, k-step kk) at
+// vb[read][d % 2] + 2048 kk + 4096 (d / 2) (keys 16 apart are two row groups
+// apart with the same swizzle)
 __device__ __forceinline__ void pv_tile(f32x16_t o[kDBlocks], const int vb[2][2],
-                                        bf16x8_t pf0, bf16x8_t pf1)
+                                        bf16x8_t pf0, bf16x8_t pf1, bf16x8_t rf0, bf16x8_t rf1)
 {
     i16x4_t vlo[kPvAhead], vhi[kPvAhead];
 #pragma unroll
@@ -482,6 +486,8 @@ __device__ __forceinline__ void pv_tile(f32x16_t o[kDBlocks], const int vb[2][2]
         const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        kk ? pf1 : pf0, o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       kk ? rf1 : rf0, o[d], 0, 0, 0);
         const int nj = j + kPvAhead;
         if (nj < 2 * kDBlocks) {
             const int nd = nj >> 1, nkk = nj & 1, off = 2048 * nkk + 4096 * (nd >> 1);
@@ -496,7 +502,7 @@ __device__ __forceinline__ void pv_tile(f32x16_t o[kDBlocks], const int vb[2][2]
 struct WideRow {
     float m;    // exponent origin (log2 units), -inf before the first visible key
     float l;    // this lane's share of sum 2^(s - m) (gives the lse)
-    float lr;   // the same over the bf16-rounded weights (normalizes the output)
+    float lr;   // the same over the weights as fed (normalizes the output)
 };
 
 // the value of x in the other half of the wave (lane ^ 32), summed or maxed
@@ -637,7 +643,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
 
             // P^T operands of the previous tile (zero before the first: that
             // iteration's value product adds nothing)
-            bf16x8_t pp0 = {}, pp1 = {};
+            bf16x8_t pp0 = {}, pp1 = {}, rp0 = {}, rp1 = {};
             bool low_any = false;         // some row of the wave outgrew its origin
             float mrun = -INFINITY;       // running maximum of the row's scores
             for (int t = 0; t < ntiles; ++t) {
@@ -681,7 +687,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                     // matrix unit works.  The schedule barriers keep that order.
                     float tmax = -INFINITY, m_use = 0.f;
                     float ex[16];
-                    uint32_t pw[8];
+                    uint32_t pw[8], pr[8];
                     i16x4_t vlo[kPvAhead], vhi[kPvAhead];
 #pragma unroll
                     for (int j = 0; j < kPvAhead; ++j) pv_read(vb, pv_block(j), pv_kstep(j), vlo[j], vhi[j]);
@@ -693,6 +699,8 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                             const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                             o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                                 __builtin_bit_cast(bf16x8_t, a), kk ? pp1 : pp0, o[d], 0, 0, 0);
+                            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(bf16x8_t, a), kk ? rp1 : rp0, o[d], 0, 0, 0);
                         }
                         if (j + kPvAhead < 2 * kDBlocks)
                             pv_read(vb, pv_block(j + kPvAhead), pv_kstep(j + kPvAhead),
@@ -718,15 +726,24 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                         } else if (j < 20) {
                             const int r = j - 5;
                             st.l += ex[r] + ex[r + 1];
-                            pw[r >> 1] = pack_bf16x2(ex[r], ex[r + 1]);
+                            const uint32_t w = pack_bf16x2(ex[r], ex[r + 1]);
+                            pw[r >> 1] = w;
                             st.lr = __builtin_amdgcn_fdot2_f32_bf16(
-                                __builtin_bit_cast(bf16x2_t, pw[r >> 1]),
+                                __builtin_bit_cast(bf16x2_t, w),
+                                __builtin_bit_cast(bf16x2_t, 0x3F803F80u), st.lr, false);
+                            // the rounding residual, exact in fp32, as the second term
+                            const uint32_t q = pack_bf16x2(ex[r] - bf16_lo(w), ex[r + 1] - bf16_hi(w));
+                            pr[r >> 1] = q;
+                            st.lr = __builtin_amdgcn_fdot2_f32_bf16(
+                                __builtin_bit_cast(bf16x2_t, q),
                                 __builtin_bit_cast(bf16x2_t, 0x3F803F80u), st.lr, false);
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     pp0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]});
                     pp1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4], pw[5], pw[6], pw[7]});
+                    rp0 = __builtin_bit_cast(bf16x8_t, u32x4_t{pr[0], pr[1], pr[2], pr[3]});
+                    rp1 = __builtin_bit_cast(bf16x8_t, u32x4_t{pr[4], pr[5], pr[6], pr[7]});
                 }
 
                 // next stages: K moves to tile t + 1, V to tile t
@@ -738,7 +755,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                 for (int j = 0; j < 4; ++j) vb[j >> 1][j & 1] += vstep;
             }
             // the last tile's value product (its softmax ran in the last iteration)
-            if (has_rows) pv_tile(o, vb, pp0, pp1);
+            if (has_rows) pv_tile(o, vb, pp0, pp1, rp0, rp1);
             if (low_any) redo = 1;
             // drain the DMA pipeline; every wave sees the same redo flag
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
