@@ -40,6 +40,9 @@ constexpr int kVStride = kDv + 16;    // bf16 per staged value row (1056 B)
 constexpr int kOStride = kDv + 16;    // fp32 per merge row
 constexpr int kStageBytes = kWaves * 16 * kVStride * 2;   // 67584
 constexpr int kMergeBytes = kWaves * 16 * kOStride * 4;   // 135168
+// the waves' value stages are used inside the key loop, the merge rows after
+// it, in the same bytes
+static_assert(kStageBytes <= kMergeBytes, "value stages lie inside the merge area");
 constexpr int kQStride = kDqk + 8;    // bf16 per query row in LDS (1168 B: 16 rows hit distinct banks)
 constexpr int kStatBytes = kWaves * 16 * 4 * 4;   // m, l, l_rounded, pad
 constexpr int kQOffset = kMergeBytes + kStatBytes;
