@@ -1,0 +1,96 @@
+"""GPU invariants of paged MLA decode that hold exactly or in closed form, for
+both kernels (16-row tiles at h_q = 16, 128-row tiles at h_q = 128), with a
+causal two-token query and part boundaries inside sequences:
+
+* scaling the cache's 512 latent dims by 2^k and the query's latent dims by
+  2^-k leaves every score bit for bit unchanged (bf16 x bf16 products are
+  exact in fp32) and scales every value row by 2^k, so the output is the
+  unscaled output times 2^k bit for bit and the lse is unchanged;
+* a zero query scores every key 0: the output is the plain mean of the
+  visible value rows and the lse is ln(number of visible keys);
+* value rows equal to one vector v give v (up to its bf16 rounding).
+"""
+import numpy as np
+import pytest
+import torch
+
+from mla_paged_kv_02_amd import inputs as gen
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+LENS = [700, 65, 2000, 1, 129]
+
+
+def _inputs(h_q, seed):
+    return gen.make_decode(LENS, s_q=2, h_q=h_q, causal=True, seed=seed)
+
+
+def _scaled_bits(bits, k):
+    """bf16 bits times 2^k (exact: only the exponent moves; NaN stays NaN)."""
+    f = gen.bf16_bits_to_f32(bits).astype(np.float64) * 2.0 ** k
+    return gen.f32_to_bf16_bits(f.astype(np.float32))
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+@pytest.mark.parametrize("k", [12, -12])
+def test_latent_rescaling_is_exact(h_q, k):
+    x = _inputs(h_q, seed=300 + h_q)
+    out0, lse0, _, _ = gu.run_decode(gu.DeviceInputs(x))
+    y = _inputs(h_q, seed=300 + h_q)
+    y.kv[..., :512] = _scaled_bits(y.kv[..., :512], k)
+    y.q[..., :512] = _scaled_bits(y.q[..., :512], -k)
+    out1, lse1, _, _ = gu.run_decode(gu.DeviceInputs(y))
+    want = _scaled_bits(_bits(out0), k)
+    assert np.array_equal(_bits(out1), want), "output not scaled bit for bit (h_q=%d, k=%d)" % (h_q, k)
+    assert np.array_equal(lse1.cpu().numpy().view(np.uint32), lse0.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_zero_query_weights_keys_equally(h_q):
+    x = _inputs(h_q, seed=310 + h_q)
+    x.q[:] = 0
+    out, lse, _, _ = gu.run_decode(gu.DeviceInputs(x))
+    got, lg = gu.dev_to_f64(out), lse.cpu().numpy().astype(np.float64)
+    for b, n in enumerate(x.seqlens):
+        n = int(n)
+        rows = gen.bf16_bits_to_f32(
+            x.kv[x.block_table[b, :(n + 63) // 64]].reshape(-1, 576)[:n, :512]).astype(np.float64)
+        for i in range(x.s_q):
+            vis = n - x.s_q + 1 + i            # bottom-right causal alignment
+            o, l = got[b, i], lg[b, i]
+            if vis <= 0:
+                assert np.all(o == 0) and np.all(np.isneginf(l))
+                continue
+            mean = rows[:vis].mean(axis=0)
+            # every weight is exactly 1: fp32 sums of at most 2000 rows (worst
+            # case (n - 1) 2^-24 of the mean magnitude, ~1e-4 here), then one
+            # bf16 rounding of the output (at most 2^-8 relative)
+            tol = 2.0 ** -8 * np.abs(mean) + 2e-4
+            assert np.all(np.abs(o - mean[None, :]) <= tol[None, :]), (b, i)
+            assert np.max(np.abs(l - np.log(vis))) <= 1e-5, (b, i)
+
+
+@pytest.mark.parametrize("h_q", [16, 128])
+def test_constant_values_give_that_value_both_kernels(h_q):
+    x = _inputs(h_q, seed=320 + h_q)
+    v = gen.f32_to_bf16_bits(np.linspace(-3, 3, 512).astype(np.float32))
+    for b, n in enumerate(x.seqlens):
+        for j in range(int(n)):
+            x.kv[x.block_table[b, j // 64], j % 64, :512] = v
+    out, _, _, _ = gu.run_decode(gu.DeviceInputs(x))
+    got = gu.dev_to_f64(out)
+    want = gen.bf16_bits_to_f32(v).astype(np.float64)
+    for b, n in enumerate(x.seqlens):
+        for i in range(x.s_q):
+            if int(n) - x.s_q + 1 + i <= 0:   # no visible key: the empty-row convention
+                assert np.all(got[b, i] == 0)
+                continue
+            # a convex combination of copies of v: v up to fp32 rounding, then
+            # the bf16 rounding of a value next to a bf16 value
+            assert np.all(np.abs(got[b, i] - want[None, :]) <=
+                          2.0 ** -8 * np.abs(want)[None, :] + 1e-6), (b, i)
