@@ -94,11 +94,29 @@ def measured_peaks(mla, torch, dev, read_gib=2, mfma_iters=4096, reps=10):
     flops = mla.probe_mfma(mfma_iters, wg_mfma, fsink)
     t_mfma = timed(lambda: mla.probe_mfma(mfma_iters, wg_mfma, fsink))
     del buf
+    lds = {(w, d): lds_rate(mla, torch, dev, cus, w, d) for w in (1, 4, 8) for d in (4, 16)}
     return {"hbm_read_GBs": round((read_gib << 30) / t_read / 1e9, 1),
             "bf16_mfma_TFLOPs": round(flops / t_mfma / 1e12, 1),
+            "lds_read_B_per_clk_per_CU": {"%d_waves_%d_deep" % k: r[0] for k, r in lds.items()},
+            "lds_read_clk_per_KB_per_wave": {"%d_waves_%d_deep" % k: r[1] for k, r in lds.items()},
             "probe": "mla_probe_read over %d GiB, %d workgroups; mla_probe_mfma %d iters x 8 "
-                     "v_mfma_f32_32x32x16_bf16 per wave, %d workgroups of 4 waves"
-                     % (read_gib, 2 * cus, mfma_iters, wg_mfma)}
+                     "v_mfma_f32_32x32x16_bf16 per wave, %d workgroups of 4 waves; mla_probe_lds "
+                     "ds_read_b128 4 or 16 in flight per wave, one workgroup per CU, shader clock "
+                     "cycles of the slowest wave" % (read_gib, 2 * cus, mfma_iters, wg_mfma)}
+
+
+def lds_rate(mla, torch, dev, cus, waves, depth, iters=1024):
+    """LDS bytes read per shader clock per CU with `waves` waves per CU each
+    streaming ds_read_b128 with `depth` in flight (mla_probe_lds), and clocks
+    per 1 KB read per wave; medians over the workgroups of a warm second run."""
+    ticks = torch.zeros(2 * waves * cus, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        per_wg = mla.probe_lds(waves, iters, cus, ticks, depth=depth)
+        torch.cuda.synchronize()
+    cyc = ticks.view(cus, waves, 2)[:, :, 0].cpu().numpy().astype(np.float64)
+    slowest = cyc.max(axis=1)
+    return (round(float(np.median(per_wg / slowest)), 1),
+            round(float(np.median(cyc / (depth * iters))), 1))
 
 
 def bmm_bytes_flops(batch, heads, k, n, fp8w=False):

@@ -254,8 +254,8 @@ int mla_absorb_bmm_fp8w(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_
                         void *stream);
 
 /*
- * Measurement probes: the rates this device reaches on the two resources
- * the decode is bound by, so that achieved throughput can be quoted as a
+ * Measurement probes: the rates this device reaches on the resources the
+ * decode is bound by, so that achieved throughput can be quoted as a
  * fraction of what is attainable as well as of the published peaks.
  *
  * mla_probe_read: streams `bytes` of `buf` once (16-byte loads, 16 KB
@@ -269,10 +269,21 @@ int mla_absorb_bmm_fp8w(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_
  * independent accumulators, i.e. workgroups * 4 * iters * 8 * 32768 flops,
  * and writes one float per wave.
  *   sink [device] float [workgroups * 4]
- * Both are enqueued on `stream`; no device allocation.
+ * mla_probe_lds: `workgroups` workgroups (one per CU: each holds 96 KB of
+ * LDS) of `waves` waves; every wave issues iters x depth ds_read_b128 (1 KB
+ * each, `depth` in flight at a time, bank-conflict free) and writes its
+ * loop's shader clock cycles and 100 MHz real-time ticks: LDS bytes read per
+ * clock per CU = waves * iters * depth * 1024 / (the slowest wave's cycles).
+ *   waves in [1, 16]; depth 1, 2, 4, 8 or 16;
+ *   ticks [device] uint32 [workgroups * waves][2]
+ *   (cycles, ticks); sink [device] uint32 [1], written only on a fixed
+ *   improbable XOR of what was read.
+ * All are enqueued on `stream`; no device allocation.
  */
 int mla_probe_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink, void *stream);
 int mla_probe_mfma(int iters, int workgroups, float *sink, void *stream);
+int mla_probe_lds(int waves, int depth, int iters, int workgroups, uint32_t *ticks,
+                  uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -6,10 +6,10 @@ MI355X (gfx950): a C-ABI library of hand-written HIP kernels
     out, lse = decode(q, kv_cache, block_table, seqlens, meta, parts, scale=s)
 """
 from .api import (absorb_bmm, absorb_bmm_fp8w, combine, decode, decode_noalloc, default_num_parts, device_cus, get_metadata,
-                  metadata_ints, probe_mfma, probe_read, split_offsets, workspace_bytes)
+                  metadata_ints, probe_lds, probe_mfma, probe_read, split_offsets, workspace_bytes)
 from ._lib import MlaError
 
 __all__ = ["MlaError", "absorb_bmm", "absorb_bmm_fp8w", "combine", "decode", "decode_noalloc",
            "default_num_parts", "device_cus",
-           "get_metadata", "metadata_ints", "probe_mfma", "probe_read", "split_offsets",
+           "get_metadata", "metadata_ints", "probe_lds", "probe_mfma", "probe_read", "split_offsets",
            "workspace_bytes"]

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_page
 SYMBOLS = ("mla_status_str", "mla_last_error", "mla_device_cus", "mla_default_num_parts",
            "mla_metadata_ints", "mla_workspace_bytes", "mla_get_metadata", "mla_decode",
            "mla_decode_noalloc", "mla_combine", "mla_absorb_bmm", "mla_absorb_bmm_fp8w", "mla_probe_read",
-           "mla_probe_mfma")
+           "mla_probe_mfma", "mla_probe_lds")
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARG = 1
@@ -73,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.mla_probe_read.argtypes = [P, i64, i32, P, P]
     lib.mla_probe_mfma.restype = i32
     lib.mla_probe_mfma.argtypes = [i32, i32, P, P]
+    lib.mla_probe_lds.restype = i32
+    lib.mla_probe_lds.argtypes = [i32, i32, i32, i32, P, P, P]
     _lib = lib
     return lib
 

@@ -261,3 +261,20 @@ def probe_mfma(iters: int, workgroups: int, sink: torch.Tensor) -> int:
     _lib.check(_lib.load().mla_probe_mfma(int(iters), int(workgroups), sink.data_ptr(),
                                           _stream(sink)), "mla_probe_mfma")
     return int(workgroups) * 4 * int(iters) * 8 * 32768
+
+
+def probe_lds(waves: int, iters: int, workgroups: int, ticks: torch.Tensor,
+              sink: Optional[torch.Tensor] = None, depth: int = 4) -> int:
+    """Run the LDS read loop (`waves` waves in each of `workgroups`
+    workgroups, one per CU, `depth` 1 KB reads in flight per wave); ticks:
+    int32 [workgroups * waves * 2] on the device, receiving (shader cycles,
+    100 MHz ticks) per wave.  Returns the bytes each workgroup reads."""
+    _need(ticks, "ticks", torch.int32)
+    if ticks.numel() < 2 * waves * workgroups:
+        raise ValueError("ticks needs %d ints" % (2 * waves * workgroups))
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=ticks.device)
+    _lib.check(_lib.load().mla_probe_lds(int(waves), int(depth), int(iters), int(workgroups),
+                                         ticks.data_ptr(), sink.data_ptr(), _stream(ticks)),
+               "mla_probe_lds")
+    return int(waves) * int(iters) * int(depth) * 1024

@@ -397,4 +397,18 @@ int mla_probe_mfma(int iters, int workgroups, float *sink, void *stream)
                       "mfma probe launch");
 }
 
+int mla_probe_lds(int waves, int depth, int iters, int workgroups, uint32_t *ticks,
+                  uint32_t *sink, void *stream)
+{
+    if (!ticks || !sink) return fail(MLA_ERR_INVALID_ARG, "ticks and sink must be non-null");
+    if (waves < 1 || waves > 16 || iters < 1 || workgroups < 1 || workgroups > (1 << 20))
+        return fail(MLA_ERR_INVALID_ARG,
+                    "waves must be in [1, 16], iters >= 1 and workgroups in [1, 2^20]");
+    if (depth != 1 && depth != 2 && depth != 4 && depth != 8 && depth != 16)
+        return fail(MLA_ERR_INVALID_ARG, "depth must be 1, 2, 4, 8 or 16 (got %d)", depth);
+    return hip_status(mla::launch_probe_lds(waves, depth, iters, workgroups, ticks, sink,
+                                            static_cast<hipStream_t>(stream)),
+                      "lds probe launch");
+}
+
 }  // extern "C"

@@ -12,6 +12,13 @@
 // each) from register operands; the sum of the accumulators goes to
 // sink[global wave] so the chain is live.  Four waves per workgroup, one per
 // SIMD.
+//
+// lds_probe_kernel: one workgroup per CU (its LDS array leaves no room for a
+// second) of `waves` waves; after a barrier every wave issues iters x D
+// ds_read_b128 (1 KB each, 16 consecutive bytes per lane: no bank conflict),
+// D in flight at a time, and records its shader-clock cycles (s_memtime) and
+// its constant-rate ticks (s_memrealtime, 100 MHz) for the loop.  Read bytes
+// per clock per CU = waves x iters x D KB over the slowest wave's cycles.
 #include "mla_device.h"
 #include "kernels.h"
 
@@ -66,11 +73,69 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int iters, fl
     if (lane == 0) sink[blockIdx.x * (kProbeThreads / 64) + (threadIdx.x >> 6)] = s;
 }
 
+constexpr int kLdsProbeBytes = 96 * 1024;     // > 80 KB: one workgroup per CU
+constexpr int kLdsProbeWindow = 64 * 1024;    // bytes the waves read
+
+template <int D>
+__global__ __launch_bounds__(1024) void lds_probe_kernel(int iters, uint32_t *ticks, uint32_t *sink)
+{
+    __shared__ __attribute__((aligned(16))) char lds[kLdsProbeBytes];
+    typedef u32x4_t __attribute__((address_space(3))) lds_u32x4_t;
+    typedef char __attribute__((address_space(3))) lds_char_t;
+    const lds_char_t *L = (const lds_char_t *)lds;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int base = wave * D * 1024 + 16 * lane;
+    // defined contents (and the whole array in use, which keeps one
+    // workgroup per CU)
+    for (int i = threadIdx.x; i < kLdsProbeBytes / 16; i += blockDim.x)
+        *(lds_u32x4_t *)((lds_char_t *)lds + 16 * i) = u32x4_t{(uint32_t)i, 1u, 2u, 3u};
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    __syncthreads();
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+#pragma unroll 1
+    for (int it = 0; it < iters; ++it) {
+        // the window moves with the iteration, so the loads stay in the loop
+        const int off = base + (it & 15) * (D * 1024);
+        u32x4_t v[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            v[d] = *(const lds_u32x4_t *)(L + ((off + 1024 * d) & (kLdsProbeWindow - 1)));
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc ^= v[d];
+    }
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0) {
+        const int w = blockIdx.x * (blockDim.x >> 6) + wave;
+        ticks[2 * w] = (uint32_t)(c1 - c0);
+        ticks[2 * w + 1] = (uint32_t)(r1 - r0);
+    }
+    // keeps the loads live (the array is never written: its contents do not matter)
+    const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (x == 0x9E3779B9u && acc.x == 0x7F4A7C15u) sink[0] = x;
+}
+
 hipError_t launch_probe_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink,
                              hipStream_t stream)
 {
     hipLaunchKernelGGL(read_probe_kernel, dim3(workgroups), dim3(kProbeThreads), 0, stream,
                        static_cast<const u32x4_t *>(buf), bytes / 16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_lds(int waves, int depth, int iters, int workgroups, uint32_t *ticks,
+                            uint32_t *sink, hipStream_t stream)
+{
+    const dim3 grid(workgroups), block(64 * waves);
+    switch (depth) {
+    case 1: hipLaunchKernelGGL(lds_probe_kernel<1>, grid, block, 0, stream, iters, ticks, sink); break;
+    case 2: hipLaunchKernelGGL(lds_probe_kernel<2>, grid, block, 0, stream, iters, ticks, sink); break;
+    case 4: hipLaunchKernelGGL(lds_probe_kernel<4>, grid, block, 0, stream, iters, ticks, sink); break;
+    case 8: hipLaunchKernelGGL(lds_probe_kernel<8>, grid, block, 0, stream, iters, ticks, sink); break;
+    default: hipLaunchKernelGGL(lds_probe_kernel<16>, grid, block, 0, stream, iters, ticks, sink); break;
+    }
     return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 """GPU checks of the measurement probes: the read probe leaves its sink
-alone, and the MFMA loop's per-wave result matches the 32x32x16 product of
-its register operands worked out on the host."""
+alone, the MFMA loop's per-wave result matches the 32x32x16 product of its
+register operands worked out on the host, and the LDS probe reports a
+cycle count and a real-time tick count for every wave."""
 import numpy as np
 import pytest
 import torch
@@ -46,3 +47,24 @@ def test_mfma_probe_sum_matches_host_product():
     assert flops == wgs * 4 * iters * 8 * 32768
     got = sink.cpu().numpy().astype(np.float64)
     assert np.allclose(got, want, rtol=1e-5, atol=1e-6), (got, want)
+
+
+def test_lds_probe_reports_every_wave():
+    """Every wave of every workgroup writes (cycles, 100 MHz ticks); both grow
+    with the iteration count, and the implied shader clock is plausible."""
+    wgs, waves = 8, 4
+    ticks = torch.zeros(2 * wgs * waves, dtype=torch.int32, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    res = {}
+    for iters in (256, 2048):
+        ticks.zero_()
+        per_wg = mla.probe_lds(waves, iters, wgs, ticks, sink, depth=8)
+        torch.cuda.synchronize()
+        assert per_wg == waves * iters * 8 * 1024
+        t = ticks.view(wgs * waves, 2).cpu().numpy().astype(np.float64)
+        assert np.all(t > 0), t
+        res[iters] = t
+    assert np.all(res[2048][:, 0] > res[256][:, 0])
+    clock_ghz = res[2048][:, 0] / (res[2048][:, 1] * 10.0)   # cycles per 10 ns
+    assert np.all((clock_ghz > 0.3) & (clock_ghz < 4.0)), clock_ghz
+    assert int(sink.item()) == 7
