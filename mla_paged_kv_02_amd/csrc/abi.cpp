@@ -397,6 +397,16 @@ int mla_probe_mfma(int iters, int workgroups, float *sink, void *stream)
                       "mfma probe launch");
 }
 
+#if MLA_STAMPS
+// instrumented build only (not part of the public header): the buffer the
+// decode kernels write each workgroup's start and end ticks to, or null
+int mla_stamps_set(uint64_t *buf)
+{
+    if (hipError_t e = mla::set_stamps_r16(buf)) return hip_status(e, "stamps (16-row kernel)");
+    return hip_status(mla::set_stamps_wide(buf), "stamps (128-row kernel)");
+}
+#endif
+
 int mla_probe_lds(int waves, int depth, int iters, int workgroups, uint32_t *ticks,
                   uint32_t *sink, void *stream)
 {

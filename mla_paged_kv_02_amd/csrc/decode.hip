@@ -49,6 +49,26 @@ constexpr int kQOffset = kMergeBytes + kStatBytes;
 constexpr int kLdsBytes = kQOffset + 16 * kQStride * 2;   // 154880
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
+#if MLA_STAMPS
+// Instrumented build only (MLA_STAMPS=1, a separate library): each
+// workgroup's start and end in 100 MHz ticks, [workgroup][2] with workgroups
+// numbered in dispatch order (x fastest), into a buffer set by
+// mla_stamps_set; nothing is written while it is null.
+__device__ uint64_t *g_stamps_r16;
+hipError_t set_stamps_r16(uint64_t *buf)
+{
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_stamps_r16), &buf, sizeof(buf));
+}
+#define MLA_STAMP(S)                                                                      \
+    do {                                                                                  \
+        if (threadIdx.x == 0 && g_stamps_r16 != nullptr)                                 \
+            g_stamps_r16[2 * ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) + (S)] =     \
+                __builtin_amdgcn_s_memrealtime();                                         \
+    } while (0)
+#else
+#define MLA_STAMP(S) ((void)0)
+#endif
+
 
 typedef u32x4_t ChunkRegs[kQkSteps];
 
@@ -172,9 +192,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
     const int rt = blockIdx.y;
     const int R = p.s_q * p.h_q;
 
+    MLA_STAMP(0);
     const int32_t *rec = meta + part * kPartInts;
     const int s0 = rec[0];
-    if (s0 < 0) return;
+    if (s0 < 0) {
+        MLA_STAMP(1);
+        return;
+    }
     const int t0 = rec[1], s1 = rec[2], t1 = rec[3], slot0 = rec[4];
     const int32_t *split_off = meta + p.num_parts * kPartInts;
 
@@ -304,7 +328,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
         }
         __syncthreads();   // before the next segment reuses LDS
     }
+    MLA_STAMP(1);
 }
+#undef MLA_STAMP
 
 hipError_t launch_decode_r16(const DecodeParams &p, int num_parts, int row_tiles,
                              hipStream_t stream)

@@ -72,6 +72,26 @@ constexpr int kDBlocks = kDv / 32;                   // 16
 constexpr float kWOriginSlack = 64.0f;   // log2 units
 constexpr int kPvAhead = 2;              // value fragments (pairs of reads) read ahead
 
+#if MLA_STAMPS
+// Instrumented build only (MLA_STAMPS=1, a separate library): each
+// workgroup's start and end in 100 MHz ticks, [workgroup][2] with workgroups
+// numbered in dispatch order (x fastest), into a buffer set by
+// mla_stamps_set; nothing is written while it is null.
+__device__ uint64_t *g_stamps_wide;
+hipError_t set_stamps_wide(uint64_t *buf)
+{
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_stamps_wide), &buf, sizeof(buf));
+}
+#define MLA_STAMP(S)                                                                      \
+    do {                                                                                  \
+        if (threadIdx.x == 0 && g_stamps_wide != nullptr)                                 \
+            g_stamps_wide[2 * ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) + (S)] =     \
+                __builtin_amdgcn_s_memrealtime();                                         \
+    } while (0)
+#else
+#define MLA_STAMP(S) ((void)0)
+#endif
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // One wave's DMA of one tile: rows 8 wave .. 8 wave + 7, all 72 chunks, as
@@ -535,9 +555,13 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
     const int rt = blockIdx.y;
     const int R = p.s_q * p.h_q;
 
+    MLA_STAMP(0);
     const int32_t *rec = meta + part * kPartInts;
     const int s0 = rec[0];
-    if (s0 < 0) return;
+    if (s0 < 0) {
+        MLA_STAMP(1);
+        return;
+    }
     const int t0 = rec[1], s1 = rec[2], t1 = rec[3], slot0 = rec[4];
     const int32_t *split_off = meta + p.num_parts * kPartInts;
     const int lds_addr = (int)(uintptr_t)(lds_char_t *)tiles;
@@ -798,7 +822,9 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
             }
         }
     }
+    MLA_STAMP(1);
 }
+#undef MLA_STAMP
 
 hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tiles,
                               hipStream_t stream)

@@ -141,6 +141,10 @@ int set_error(int status, const char *fmt, ...);
 hipError_t launch_probe_read(const void *buf, int64_t bytes, int workgroups, uint32_t *sink,
                              hipStream_t stream);
 hipError_t launch_probe_mfma(int iters, int workgroups, float *sink, hipStream_t stream);
+#if MLA_STAMPS
+hipError_t set_stamps_r16(uint64_t *buf);
+hipError_t set_stamps_wide(uint64_t *buf);
+#endif
 hipError_t launch_probe_lds(int waves, int depth, int iters, int workgroups, uint32_t *ticks,
                             uint32_t *sink, hipStream_t stream);
 

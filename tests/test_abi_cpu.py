@@ -150,3 +150,11 @@ def test_other_validation(lib):
     assert lib.mla_probe_read(FAKE, 1 << 20, 0, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
     assert lib.mla_probe_mfma(0, 8, FAKE, None) == _lib.MLA_ERR_INVALID_ARG
     assert lib.mla_probe_mfma(16, 8, None, None) == _lib.MLA_ERR_INVALID_ARG
+
+
+def test_default_library_has_no_timing_hook(lib):
+    # per-workgroup timestamps exist only in the separately built instrumented
+    # copy; the library the tests and the benchmark load writes none
+    assert not hasattr(lib, "mla_stamps_set")
+    from mla_paged_kv_02_amd import build
+    assert build.STAMPS_LIB != _lib.LIB_PATH
