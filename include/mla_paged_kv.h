@@ -83,12 +83,10 @@ int mla_default_num_parts(int num_cus, int batch, int s_q, int h_q);
  *                      with exactly one slot is written in place.
  *   1                  total chunks (16-token units) over the batch.
  *   batch + 1          extra merge workgroups before each sequence: a
- *                      sequence with k > 32 slots gets ceil(k / 16) - 1
- *                      (exclusive prefix; the last entry is the total).
- *   batch              heavy rank: sequences with > 32 slots before b.
- *   512 * ((batch + num_parts) / 33 + 1)
- *                      merge counters, one per heavy sequence and group of
- *                      4 rows; zero except while a decode call runs. */
+ *                      sequence with k > 32 slots gets 4 S - 1, S = 2 for
+ *                      k < 64, 4 for k < 128, 8 for k < 256, else 16 (the
+ *                      dim slices each of its rows is merged in); an
+ *                      exclusive prefix, the last entry is the total. */
 size_t mla_metadata_ints(int batch, int num_parts);
 
 /* Bytes of decode workspace: fp32 partial outputs and log-sum-exps for up
@@ -150,22 +148,20 @@ int mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int nu
  *   block_table [device] int32 [batch][bt_stride]
  *   seqlens     [device] int32 [batch]
  *   metadata    [device] from mla_get_metadata with the same batch, s_q, h_q,
- *               num_parts and lengths.  The call uses its merge counters and
- *               leaves them zero again when its work completes, so the
- *               buffer can serve any number of calls in stream order; calls
- *               running concurrently on one metadata buffer race.
+ *               num_parts and lengths; read only, so one buffer can serve
+ *               any number of calls, also concurrent ones.
  *   workspace   [device] >= mla_workspace_bytes(batch, s_q, h_q, num_parts)
  *   out         [device] bf16 [batch][s_q][h_q][512]
  *   lse         [device] fp32 [batch][s_q][h_q]
  * Sequences cut into several parts are merged by the combine kernel on the
- * same stream before the call's work completes; a sequence cut into more
- * than 32 parts is merged in two levels (16 parts per workgroup, then the
- * last workgroup of each row group merges those results).
+ * same stream before the call's work completes; each row of a sequence cut
+ * into more than 32 parts is merged by several workgroups, one per slice of
+ * its 512 output dims.
  */
 int mla_decode(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
                const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens,
                int batch, int s_q, int h_q, int d_qk, int d_v, int page_size,
-               float scale, int causal, int32_t *metadata, int num_parts,
+               float scale, int causal, const int32_t *metadata, int num_parts,
                void *workspace, size_t workspace_bytes, uint16_t *out, float *lse,
                void *stream);
 
@@ -187,7 +183,7 @@ int mla_decode(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
 int mla_decode_noalloc(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
                        const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens,
                        int batch, int s_q, int h_q, int d_qk, int d_v, int page_size, float scale,
-                       int causal, int32_t *metadata, int num_parts, uint16_t *out, float *lse,
+                       int causal, const int32_t *metadata, int num_parts, uint16_t *out, float *lse,
                        void *stream);
 
 /*

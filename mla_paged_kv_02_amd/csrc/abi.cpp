@@ -150,7 +150,7 @@ int set_error(int status, const char *fmt, ...)
 int decode_call(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
                 const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens, int batch,
                 int s_q, int h_q, int d_qk, int d_v, int page_size, float scale, int causal,
-                int32_t *metadata, int num_parts, const WorkspaceSource &ws, uint16_t *out,
+                const int32_t *metadata, int num_parts, const WorkspaceSource &ws, uint16_t *out,
                 float *lse, void *stream)
 {
     if (!q || !kv_cache || !block_table || !seqlens || !metadata || !out || !lse)
@@ -224,15 +224,13 @@ int decode_call(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
                              : mla::launch_decode_r16(p, num_parts, row_tiles, st);
     if (e != hipSuccess) return hip_status(e, "decode kernel launch");
 
-    // the merge may rewrite partials and counters in place (see combine.hip)
+    // heavily split sequences get the schedule's extra merge workgroups
     const mla::MetaLayout L{batch, num_parts};
     mla::CombineParams c;
     c.o_part = o_part;
     c.lse_part = lse_part;
     c.split_off = metadata + L.split_off();
     c.extra_off = metadata + L.extra_off();
-    c.heavy_rank = metadata + L.heavy_rank();
-    c.counters = metadata + L.counters();
     c.rows = rows;
     c.skip_single = 1;
     c.out = out;
@@ -315,7 +313,7 @@ int mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int nu
 int mla_decode(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
                const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens,
                int batch, int s_q, int h_q, int d_qk, int d_v, int page_size,
-               float scale, int causal, int32_t *metadata, int num_parts,
+               float scale, int causal, const int32_t *metadata, int num_parts,
                void *workspace, size_t workspace_bytes, uint16_t *out, float *lse,
                void *stream)
 {
@@ -337,12 +335,10 @@ int mla_combine(const float *o_part, const float *lse_part, const int32_t *split
     if (!aligned(o_part, 16) || !aligned(out, 16))
         return fail(MLA_ERR_INVALID_ARG, "o_part and out must be 16-byte aligned");
     mla::CombineParams c;
-    c.o_part = const_cast<float *>(o_part);   // read only on this path
-    c.lse_part = const_cast<float *>(lse_part);
+    c.o_part = o_part;
+    c.lse_part = lse_part;
     c.split_off = split_offsets;
-    c.extra_off = nullptr;   // one-level merge: inputs stay untouched
-    c.heavy_rank = nullptr;
-    c.counters = nullptr;
+    c.extra_off = nullptr;   // no schedule: four waves per row of a heavy sequence
     c.rows = s_q * h_q;
     c.skip_single = 0;
     c.out = out;

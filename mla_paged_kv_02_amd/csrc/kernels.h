@@ -27,13 +27,12 @@ struct DecodeParams {
 };
 
 struct CombineParams {
-    float *o_part;              // the two-level merge rewrites some partials in place
-    float *lse_part;
+    const float *o_part;
+    const float *lse_part;
     const int32_t *split_off;   // [batch + 1]
-    // two-level merge of heavily split sequences (null: one level)
-    const int32_t *extra_off;   // [batch + 1] extra workgroups before each sequence
-    const int32_t *heavy_rank;  // [batch] heavy sequences before each sequence
-    int32_t *counters;          // [heavy rank * kRowGroupsMax + row group], zero between calls
+    // sliced merge of heavily split sequences inside a decode call: extra
+    // workgroups before each sequence [batch + 1] (null: the standalone merge)
+    const int32_t *extra_off;
     int rows;                   // s_q * h_q
     int skip_single;            // rows of single-split sequences are already final
     uint16_t *out;
@@ -54,12 +53,18 @@ struct AbsorbParams {
     int heads;
 };
 
-// Sequences split more than kFewSplits ways are "heavy": with the two-level
-// merge, kHeavyChunk consecutive splits are merged per workgroup first.
+// Sequences split more than kFewSplits ways are "heavy": inside a decode
+// call each row of one is merged by heavy_slices(k) workgroups, one per slice
+// of 512 / heavy_slices(k) output dims (see combine.hip).
 constexpr int kFewSplits = 32;
-constexpr int kHeavyChunk = 16;
 constexpr int kCombineRows = 4;                 // rows per combine workgroup
-constexpr int kRowGroupsMax = 2048 / kCombineRows;   // s_q * h_q <= 16 * 128
+// dim slices for a heavy sequence with k slots: 2 for 33..63, 4 from 64, 8
+// from 128, 16 from 256; so its kCombineRows * slices workgroups per row
+// group are at most k / 4
+__host__ __device__ constexpr int heavy_slices(int k)
+{
+    return k >= 256 ? 16 : k >= 128 ? 8 : k >= 64 ? 4 : 2;
+}
 
 constexpr int kPartInts = 8;          // ints per scheduler-part record
 constexpr int kMetaMaxBatch = 8192;
@@ -70,22 +75,18 @@ constexpr int kMaxSeqLen = 1 << 21;
 constexpr int kMaxParts = 65536;
 
 // Offsets (in int32) of the metadata sections for batch B and P parts:
-// part records, split offsets [B + 1], total chunks, extra combine
-// workgroups before each sequence [B + 1], heavy rank of each sequence [B],
-// and the merge counters (zero whenever no decode call is running).
+// part records, split offsets [B + 1], total chunks, and the extra combine
+// workgroups before each sequence [B + 1].
 struct MetaLayout {
     int64_t B, P;
     __host__ __device__ int64_t split_off() const { return kPartInts * P; }
     __host__ __device__ int64_t total_chunks() const { return split_off() + B + 1; }
     __host__ __device__ int64_t extra_off() const { return total_chunks() + 1; }
-    __host__ __device__ int64_t heavy_rank() const { return extra_off() + B + 1; }
-    __host__ __device__ int64_t counters() const { return heavy_rank() + B; }
-    // a heavy sequence has more than kFewSplits of the < B + P splits
-    __host__ __device__ int64_t heavy_max() const { return (B + P) / (kFewSplits + 1) + 1; }
-    __host__ __device__ int64_t ints() const { return counters() + kRowGroupsMax * heavy_max(); }
-    // extra combine workgroups per row group: sum over heavy b of
-    // ceil(ns_b / kHeavyChunk) - 1 <= (B + P) / kHeavyChunk
-    __host__ __device__ int64_t extra_max() const { return (B + P) / kHeavyChunk + 1; }
+    __host__ __device__ int64_t ints() const { return extra_off() + B + 1; }
+    // extra combine workgroups per row group: a heavy sequence with k slots
+    // has kCombineRows * heavy_slices(k) - 1 <= k / 4, and the slots of all
+    // sequences number fewer than B + P
+    __host__ __device__ int64_t extra_max() const { return (B + P) / 4 + 1; }
 };
 
 hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int lead,
@@ -116,7 +117,7 @@ constexpr int schedule_lead(int rows)
 }
 hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tiles,
                               hipStream_t stream);
-// `extra_wgs`: upper bound on the extra workgroups of the two-level merge
+// `extra_wgs`: upper bound on the extra workgroups of heavily split sequences
 hipError_t launch_combine(const CombineParams &p, int batch, int extra_wgs, hipStream_t stream);
 hipError_t launch_absorb(const AbsorbParams &p, int heads, hipStream_t stream);
 // Where mla_decode's partial results go: the caller's workspace (ptr, bytes),
@@ -133,7 +134,7 @@ struct WorkspaceSource {
 int decode_call(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
                 const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens, int batch,
                 int s_q, int h_q, int d_qk, int d_v, int page_size, float scale, int causal,
-                int32_t *metadata, int num_parts, const WorkspaceSource &ws, uint16_t *out,
+                const int32_t *metadata, int num_parts, const WorkspaceSource &ws, uint16_t *out,
                 float *lse, void *stream);
 // Record a failure reason for mla_last_error(); returns `status`.
 int set_error(int status, const char *fmt, ...);

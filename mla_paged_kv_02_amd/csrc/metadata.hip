@@ -17,9 +17,8 @@
 // unit x is floor(((x+1)*U - 1) / TC).  A sequence touched by k parts gets k
 // partial-result slots (k = 1: written in place by the decode kernel).
 // A sequence with more than kFewSplits slots is "heavy": the decode call's
-// merge gives it ceil(k / kHeavyChunk) workgroups per row group, the extra
-// ones numbered after all sequences (extra_off), and a counter per row group
-// (indexed by its heavy rank) that this kernel zeroes.
+// merge gives it kCombineRows * heavy_slices(k) workgroups per row group, the
+// extra ones numbered after all sequences (extra_off).
 //
 // One workgroup of 256 threads; lengths are read on the device once (the
 // per-sequence data lives in LDS), so a serving loop needs no host
@@ -165,38 +164,21 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *s
     for (int b = t; b <= batch; b += kMetaThreads) split_off[b] = splits[b];
     if (t == 0) meta[L.total_chunks()] = total;
 
-    // heavy sequences: extra merge workgroups and ranks
-    int local_x = 0, local_h = 0;
+    // heavy sequences: extra merge workgroups
+    int local_x = 0;
     for (int b = b0; b < b1; ++b) {
         const int ns = splits[b + 1] - splits[b];
-        if (ns > kFewSplits) {
-            local_x += (ns + kHeavyChunk - 1) / kHeavyChunk - 1;
-            local_h += 1;
-        }
+        if (ns > kFewSplits) local_x += kCombineRows * heavy_slices(ns) - 1;
     }
-    int total_x = 0, total_h = 0, run_x = 0, run_h = 0;   // extra workgroups, heavy sequences
-    block_exclusive_scan2(local_x, local_h, scratch[2], run_x, run_h, total_x, total_h);
+    int total_x = 0, run_x = 0, unused_run2 = 0, unused_total2 = 0;
+    block_exclusive_scan2(local_x, 0, scratch[2], run_x, unused_run2, total_x, unused_total2);
     int32_t *extra_off = meta + L.extra_off();
-    int32_t *heavy_rank = meta + L.heavy_rank();
     for (int b = b0; b < b1; ++b) {
         const int ns = splits[b + 1] - splits[b];
         extra_off[b] = run_x;
-        heavy_rank[b] = run_h;
-        if (ns > kFewSplits) {
-            run_x += (ns + kHeavyChunk - 1) / kHeavyChunk - 1;
-            run_h += 1;
-        }
+        if (ns > kFewSplits) run_x += kCombineRows * heavy_slices(ns) - 1;
     }
     if (t == 0) extra_off[batch] = total_x;
-    // all merge counters start at zero (16-byte stores where aligned)
-    int32_t *counters = meta + L.counters();
-    const int64_t nc = kRowGroupsMax * L.heavy_max();
-    const int64_t head = min(nc, (-(L.counters())) & 3);   // ints before a 16-byte boundary
-    for (int64_t i = t; i < head; i += kMetaThreads) counters[i] = 0;
-    for (int64_t i = head + 4 * (int64_t)t; i + 4 <= nc; i += 4 * kMetaThreads)
-        *reinterpret_cast<int4 *>(counters + i) = make_int4(0, 0, 0, 0);
-    for (int64_t i = head + ((nc - head) & ~(int64_t)3) + t; i < nc; i += kMetaThreads)
-        counters[i] = 0;
 
     for (int part = t; part < num_parts; part += kMetaThreads) {
         int32_t *rec = meta + part * kPartInts;

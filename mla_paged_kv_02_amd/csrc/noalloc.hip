@@ -9,8 +9,8 @@
 // the device address of each device's copy comes from hipGetSymbolAddress,
 // called once per device with that device current, and only that address is
 // handed to the kernels.  The decode writes every partial it reads in the
-// same call (the merge counters live in the caller's metadata), so nothing in
-// the array has to start at zero and no clearing is needed.  All calls on one
+// same call, so nothing in the array has to start at zero and no clearing is
+// needed.  All calls on one
 // device share its array: calls that overlap in time on one device race.
 #include <hip/hip_runtime.h>
 
@@ -58,7 +58,7 @@ extern "C" {
 int mla_decode_noalloc(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
                        const int32_t *block_table, int64_t bt_stride, const int32_t *seqlens,
                        int batch, int s_q, int h_q, int d_qk, int d_v, int page_size, float scale,
-                       int causal, int32_t *metadata, int num_parts, uint16_t *out, float *lse,
+                       int causal, const int32_t *metadata, int num_parts, uint16_t *out, float *lse,
                        void *stream)
 {
     mla::WorkspaceSource ws;

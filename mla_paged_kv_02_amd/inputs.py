@@ -209,14 +209,23 @@ def make_decode(seqlens, *, s_q: int, h_q: int, causal: bool, seed: int,
                         causal=causal, name=name)
 
 
+def config_shape(name: str, seed: Optional[int] = None):
+    """(seqlens, s_q, h_q, causal) of a named workload: the lengths make_config
+    draws with the same seed, without building its cache."""
+    if seed is None:
+        seed = 1000 + CONFIG_INDEX[name]
+    rng_len = np.random.default_rng(np.random.SeedSequence(seed).spawn(5)[0])
+    s_q, h_q, causal = _SHAPES[name]
+    return _lengths(name, rng_len), s_q, h_q, causal
+
+
 def make_config(name: str, seed: Optional[int] = None) -> DecodeInputs:
     """One of the named workloads; seed defaults to 1000 + its index."""
     if seed is None:
         seed = 1000 + CONFIG_INDEX[name]
     ss = np.random.SeedSequence(seed).spawn(5)
-    rng_len, rng_perm, rng_q, rng_kv, rng_w = (np.random.default_rng(s) for s in ss)
-    s_q, h_q, causal = _SHAPES[name]
-    seqlens = _lengths(name, rng_len)
+    rng_perm, rng_q, rng_kv, rng_w = (np.random.default_rng(s) for s in ss[1:])
+    seqlens, s_q, h_q, causal = config_shape(name, seed)
     kv, bt = paged_cache(seqlens, rng_perm, rng_kv)
     if name in ("full_step", "full_step_fp8"):
         B, H = len(seqlens), h_q

@@ -10,8 +10,12 @@ numbered in dispatch order, x fastest, and consecutive numbers go to the
 eight XCDs in turn, so number mod 8 is the XCD.  For each call the script
 measures times from the first start and prints, as one JSON line, medians
 over the calls of: the kernel span (last end), the median workgroup end,
-the tail (last end minus median end), the median workgroup duration, and
-per XCD the median and last end.
+the tail (last end minus median end), the median workgroup duration, per
+XCD the median and last end, and the whole mla_decode call (decode and
+merge kernels) timed with HIP events on its stream.  As in the benchmark,
+consecutive calls read different copies of the cache (at least 1 GiB in
+all), so the last-level cache does not serve a call what the previous one
+read.
 """
 from __future__ import annotations
 
@@ -51,6 +55,8 @@ def main(argv=None) -> int:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
     q, kv = to_dev(x.q), to_dev(x.kv)
+    replicas = max(2, int(np.ceil((1 << 30) / kv.numel() / 2)))
+    kvs = [kv] + [kv.clone() for _ in range(replicas - 1)]
     bt = torch.from_numpy(x.block_table).to(dev)
     seqlens = torch.from_numpy(x.seqlens).to(dev)
     parts = args.num_parts or api.default_num_parts(x.batch, x.s_q, x.h_q, 0)
@@ -60,14 +66,23 @@ def main(argv=None) -> int:
     stamps = torch.zeros(2 * wgs, dtype=torch.int64, device=dev)
     _lib.check(lib.mla_stamps_set(stamps.data_ptr()), "mla_stamps_set")
     meta, parts = api.get_metadata(seqlens, x.s_q, x.h_q, parts)
-    spans, meds, tails, durs, per_xcd = [], [], [], [], []
+    out = torch.empty((x.batch, x.s_q, x.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((x.batch, x.s_q, x.h_q), dtype=torch.float32, device=dev)
+    ws = torch.empty(api.workspace_bytes(x.batch, x.s_q, x.h_q, parts), dtype=torch.uint8,
+                     device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spans, meds, tails, durs, per_xcd, calls = [], [], [], [], [], []
     try:
         for i in range(args.reps + 2):
             stamps.zero_()
-            api.decode(q, kv, bt, seqlens, meta, parts, scale=x.scale, causal=x.causal)
+            e0.record()
+            api.decode(q, kvs[i % replicas], bt, seqlens, meta, parts, scale=x.scale,
+                       causal=x.causal, workspace=ws, out=out, lse=lse)
+            e1.record()
             torch.cuda.synchronize()
             if i < 2:
                 continue                                 # warm-up calls
+            calls.append(e0.elapsed_time(e1) * 1e3)
             raw = stamps.cpu().numpy().reshape(-1, 2)
             ids = np.nonzero(raw[:, 0] > 0)[0]                  # launched workgroups only
             t = raw[ids].astype(np.float64) / 100.0             # 100 MHz ticks -> µs
@@ -84,6 +99,8 @@ def main(argv=None) -> int:
     px = np.median(np.array(per_xcd), axis=0)
     print(json.dumps({
         "config": args.config, "workgroups": int(len(ids)), "calls": args.reps,
+        "cache_replicas": replicas,
+        "call_us": round(float(np.median(calls)), 2),
         "span_us": round(float(np.median(spans)), 2),
         "median_end_us": round(float(np.median(meds)), 2),
         "tail_us": round(float(np.median(tails)), 2),

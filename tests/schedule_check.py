@@ -14,9 +14,8 @@ import numpy as np
 
 CHUNK = 16
 WIDE_ROWS = 128
-FEW_SPLITS = 32        # more splits than this: two-level merge
-HEAVY_CHUNK = 16       # splits per first-level merge workgroup
-ROW_GROUPS_MAX = 512   # merge counters per heavy sequence
+FEW_SPLITS = 32        # more splits than this: a heavy sequence
+COMBINE_ROWS = 4       # rows per merge workgroup
 
 
 MAX_SEQ_LEN = 1 << 21  # lengths are capped here on the device
@@ -69,15 +68,15 @@ def expected_metadata(seqlens, num_parts, lead):
         recs[p, 3] = min((i1 + 1) * CHUNK, n[s1])
         first_part_of_s0 = min(q for q in range(P) if any(c[0] == s0 for c in chunks[q]))
         recs[p, 4] = split_off[s0] + (p - first_part_of_s0)
-    # merge sections: extra workgroups of heavy (> 32-way split) sequences,
-    # their ranks, zeroed counters
-    heavy = nsplit > FEW_SPLITS
-    extra = np.where(heavy, (nsplit + HEAVY_CHUNK - 1) // HEAVY_CHUNK - 1, 0)
-    extra_off = np.concatenate([[0], np.cumsum(extra)])
-    heavy_rank = np.concatenate([[0], np.cumsum(heavy)])[:B]
-    counters = np.zeros(ROW_GROUPS_MAX * ((B + P) // (FEW_SPLITS + 1) + 1), dtype=np.int64)
-    return np.concatenate([recs.ravel(), split_off, [int(ch.sum())], extra_off, heavy_rank,
-                           counters]).astype(np.int32)
+    # merge section: extra workgroups of heavy (> 32-way split) sequences,
+    # 4 rows x S dim slices per row group, S by the header's table
+    def slices(k):
+        return 16 if k >= 256 else 8 if k >= 128 else 4 if k >= 64 else 2
+
+    extra = [COMBINE_ROWS * slices(int(k)) - 1 if k > FEW_SPLITS else 0 for k in nsplit]
+    extra_off = np.concatenate([[0], np.cumsum(extra, dtype=np.int64)])
+    return np.concatenate([recs.ravel(), split_off, [int(ch.sum())],
+                           extra_off]).astype(np.int32)
 
 
 def check_valid(meta, seqlens, num_parts):
@@ -112,3 +111,57 @@ def check_valid(meta, seqlens, num_parts):
     for s in range(B):
         want = list(range(split_off[s], split_off[s + 1]))
         assert slots_seen[s] == want, (s, slots_seen[s], want)
+
+
+def segment_costs(meta, seqlens, num_parts, cost):
+    """Per non-empty part: its 16-token chunks plus `cost` for every sequence
+    segment it runs (query load, pipeline fill and result write, in chunks)."""
+    n = capped(seqlens)
+    P = int(num_parts)
+    recs = np.asarray(meta, dtype=np.int64)[:8 * P].reshape(P, 8)
+    out = []
+    for p in range(P):
+        s0, t0, s1, t1 = (int(v) for v in recs[p, :4])
+        if s0 < 0:
+            continue
+        c = 0
+        for s in range(s0, s1 + 1):
+            a = t0 if s == s0 else 0
+            e = t1 if s == s1 else int(n[s])
+            if a < e:
+                c += cost + (e + CHUNK - 1) // CHUNK - a // CHUNK
+        out.append(c)
+    return np.array(out, dtype=np.int64)
+
+
+def best_max_cost(seqlens, num_parts, cost):
+    """The smallest possible largest part cost (segment_costs) over all cuts of
+    the chunk list, in order, into at most num_parts runs.  For a bound T,
+    filling each part as far as T allows uses the fewest parts (taking more of
+    the next sequence into a part never makes a later part costlier), so a
+    binary search over T with that greedy count gives the optimum."""
+    ch = [int(c) for c in (capped(seqlens) + CHUNK - 1) // CHUNK if c]
+    if not ch:
+        return 0
+
+    def parts_needed(T):
+        used, cur = 1, 0
+        for rem in ch:
+            while rem:
+                if cur + cost + 1 > T:      # not even one chunk fits: next part
+                    used, cur = used + 1, 0
+                take = min(rem, T - cur - cost)
+                cur += cost + take
+                rem -= take
+                if rem:
+                    used, cur = used + 1, 0
+        return used
+
+    lo, hi = cost + 1, sum(ch) + cost * len(ch)
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if parts_needed(mid) <= num_parts:
+            hi = mid
+        else:
+            lo = mid + 1
+    return lo

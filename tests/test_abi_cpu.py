@@ -42,8 +42,8 @@ def test_status_strings(lib):
 
 
 def test_sizes(lib):
-    # records, split offsets, total, extra merge offsets, heavy ranks, counters
-    assert lib.mla_metadata_ints(64, 256) == 8 * 256 + (64 + 1) + 1 + (64 + 1) + 64 + 512 * 10
+    # records, split offsets, total, extra merge offsets
+    assert lib.mla_metadata_ints(64, 256) == 8 * 256 + (64 + 1) + 1 + (64 + 1)
     assert lib.mla_workspace_bytes(64, 1, 16, 256) == (64 + 256) * 16 * 513 * 4
     assert lib.mla_default_num_parts(256, 64, 1, 16) == 256
     assert lib.mla_default_num_parts(256, 128, 2, 128) == 128   # two 128-row tiles

@@ -427,11 +427,12 @@ def test_debug_checks_reject_out_of_range_tables(monkeypatch):
                                             ("skewed", None), ("tiny", 7)])
 def test_merge_reads_fresh_partials(name, num_parts):
     """Split sequences' partials are written and read back inside every call
-    (the heavy sequence of the skewed workload also merged in two levels, in
-    place).  The workspace is filled with NaN before every other call and
-    with finite garbage in between, so a partial read before it was written,
-    or a stale one, shows up as a NaN or a changed bit; twenty calls must
-    give bitwise the same result, and leave the merge counters at zero."""
+    (the heavy sequence of the skewed workload merged in dim slices by the
+    schedule's extra workgroups).  The workspace is filled with NaN before
+    every other call and with finite garbage in between, so a partial read
+    before it was written, or a stale one, shows up as a NaN or a changed
+    bit; twenty calls must give bitwise the same result and leave the
+    metadata as the schedule wrote it."""
     x = gen.make_config(name)
     d = gu.DeviceInputs(x)
     meta, parts = mla.get_metadata(d.seqlens, x.s_q, x.h_q, num_parts)
@@ -449,7 +450,7 @@ def test_merge_reads_fresh_partials(name, num_parts):
         else:
             assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16)), "call %d" % i
             assert torch.equal(lse, ref[1]), "call %d" % i
-    # the counters are back to zero: the metadata equals a fresh schedule
+    # the decode only reads the metadata: it equals a fresh schedule
     fresh, _ = mla.get_metadata(d.seqlens, x.s_q, x.h_q, parts)
     torch.cuda.synchronize()
     assert torch.equal(meta, fresh)

@@ -1,8 +1,8 @@
 """The decode step captured into a HIP graph (torch.cuda.CUDAGraph): every
 replay, with eager work of the program between replays, gives bitwise the
-eager result.  The schedule's merge counters are cleared by a kernel, never
-by a memset, so nothing in the captured step depends on state left by the
-previous replay."""
+eager result.  The captured step holds no memset and the decode keeps no
+state between calls (the metadata is only read), so nothing in a replay
+depends on what the previous replay left."""
 import numpy as np
 import pytest
 import torch

@@ -1,7 +1,11 @@
-"""The documented split schedule, re-derived in Python, is itself valid."""
+"""The documented split schedule, re-derived in Python, is itself valid, and
+its cuts are close to the best contiguous ones under a per-segment cost."""
+import itertools
+
 import numpy as np
 import pytest
 
+from mla_paged_kv_02_amd import inputs as gen
 from tests import schedule_check as sc
 
 CASES = [
@@ -61,3 +65,43 @@ def test_checker_rejects_broken_schedules():
     bad[8 * parts + 1] += 1     # split offsets inconsistent with the parts
     with pytest.raises(AssertionError):
         sc.check_valid(bad, seqlens, parts)
+
+
+def _brute_best(seqlens, parts, cost):
+    """All cuts of the chunk list into at most `parts` runs, by enumeration."""
+    ch = (np.maximum(np.asarray(seqlens), 0) + 15) // 16
+    units = [(b, i) for b in range(len(ch)) for i in range(int(ch[b]))]
+    best = None
+    for k in range(min(parts, len(units))):
+        for cuts in itertools.combinations(range(1, len(units)), k):
+            bounds = (0,) + cuts + (len(units),)
+            worst = max(len(units[a:e]) + cost * len({b for b, _ in units[a:e]})
+                        for a, e in zip(bounds, bounds[1:]))
+            best = worst if best is None else min(best, worst)
+    return best
+
+
+@pytest.mark.parametrize("cost", [0, 1, 3])
+@pytest.mark.parametrize("seqlens,parts", [([40, 100, 17], 2), ([40, 100, 17], 3),
+                                           ([16, 16, 16, 16], 3), ([90, 0, 33, 60], 4),
+                                           ([129], 3), ([1, 200, 1], 2)])
+def test_best_max_cost_matches_enumeration(seqlens, parts, cost):
+    assert sc.best_max_cost(seqlens, parts, cost) == _brute_best(seqlens, parts, cost)
+
+
+@pytest.mark.parametrize("name", ["memory_bound", "compute_bound", "skewed", "full_step",
+                                  "multi_token_4", "multi_token_8", "len_1k", "len_5k"])
+def test_cuts_near_best_partition(name):
+    """With the per-sequence lead as the cost of every segment, the unit cuts
+    land within 3% (or two chunks) of the best largest part over all
+    contiguous cuts into the same number of parts (at 256 compute units): a
+    better cut rule has little to gain on these workloads."""
+    seqlens, s_q, h_q, _ = gen.config_shape(name)
+    rows = s_q * h_q
+    tiles = (rows + 127) // 128 if rows >= 48 else (rows + 15) // 16
+    parts = 256 // tiles
+    lead = sc.lead_for(s_q, h_q)
+    meta = sc.expected_metadata(seqlens, parts, lead)
+    got = int(sc.segment_costs(meta, seqlens, parts, lead).max())
+    best = sc.best_max_cost(seqlens, parts, lead)
+    assert best <= got <= best + max(0.03 * best, 2), (got, best)
