@@ -99,12 +99,16 @@ size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts);
  * serving batches of sequences of differing lengths as its target).  Reads
  * the sequence lengths on the device (no host synchronization) and cuts the
  * sequences, in batch order, into `num_parts` contiguous ranges of near-equal
- * cost, where a sequence costs its 16-token chunks plus a fixed lead of C
- * chunks for starting it (with R = s_q * h_q: C = 8 when R = 128, 24 when
- * R > 128, else 16): with TC cost units in all and U = min(num_parts, TC), part p < U takes
- * the chunks whose units fall in [floor(p*TC/U), floor((p+1)*TC/U)), chunk i
- * of sequence b sitting at unit (units of the sequences before b) + C + i.
- * A part whose range holds lead units only is empty.  Writes the metadata
+ * cost, where a sequence costs its 16-token chunks plus a lead of C chunks
+ * for starting it: with TC cost units in all and U = min(num_parts, TC),
+ * part p < U takes the chunks whose units fall in [floor(p*TC/U),
+ * floor((p+1)*TC/U)), chunk i of sequence b sitting at unit (units of the
+ * sequences before b) + C + i.  A part whose range holds lead units only is
+ * empty.  With R = s_q * h_q, let S = 16 when R is 16 or 32 (the 16-row
+ * kernel) and S = 24 otherwise (the 128-row kernel): S prices one segment
+ * (a part's run of one sequence) in chunks.  For 16 or 32 rows C = S; for
+ * more, C is 0 or S, whichever gives the smaller largest part when every
+ * part costs its chunks plus S per segment (ties: S).  Writes the metadata
  * described above.  Compute once per decode step; it stays valid for every
  * layer while the lengths do not change.
  *   seqlens  [device] int32 [batch]; a negative length counts as 0 and one

@@ -304,8 +304,9 @@ int mla_get_metadata(const int32_t *seqlens, int batch, int s_q, int h_q, int nu
     if (num_parts < 1 || num_parts > mla::kMaxParts)
         return fail(MLA_ERR_INVALID_ARG, "num_parts must be in [1, %d] (got %d)", mla::kMaxParts,
                     num_parts);
-    return hip_status(mla::launch_metadata(seqlens, batch, num_parts,
-                                           mla::schedule_lead(s_q * h_q), metadata,
+    const int rows = s_q * h_q;
+    return hip_status(mla::launch_metadata(seqlens, batch, num_parts, mla::segment_cost(rows),
+                                           mla::use_wide(rows), metadata,
                                            static_cast<hipStream_t>(stream)),
                       "metadata kernel launch");
 }
@@ -395,7 +396,8 @@ int mla_probe_mfma(int iters, int workgroups, float *sink, void *stream)
 
 #if MLA_STAMPS
 // instrumented build only (not part of the public header): the buffer the
-// decode kernels write each workgroup's start and end ticks to, or null
+// decode kernels write each workgroup's timing record to (layout in
+// stamps.h), or null
 int mla_stamps_set(uint64_t *buf)
 {
     if (hipError_t e = mla::set_stamps_r16(buf)) return hip_status(e, "stamps (16-row kernel)");

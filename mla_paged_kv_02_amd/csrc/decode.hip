@@ -28,6 +28,7 @@
 //    partial for the split-KV merge.
 #include "mla_device.h"
 #include "kernels.h"
+#include "stamps.h"
 
 namespace mla {
 
@@ -50,23 +51,12 @@ constexpr int kLdsBytes = kQOffset + 16 * kQStride * 2;   // 154880
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 #if MLA_STAMPS
-// Instrumented build only (MLA_STAMPS=1, a separate library): each
-// workgroup's start and end in 100 MHz ticks, [workgroup][2] with workgroups
-// numbered in dispatch order (x fastest), into a buffer set by
-// mla_stamps_set; nothing is written while it is null.
+// Instrumented build only: the record buffer of stamps.h, or null.
 __device__ uint64_t *g_stamps_r16;
 hipError_t set_stamps_r16(uint64_t *buf)
 {
     return hipMemcpyToSymbol(HIP_SYMBOL(g_stamps_r16), &buf, sizeof(buf));
 }
-#define MLA_STAMP(S)                                                                      \
-    do {                                                                                  \
-        if (threadIdx.x == 0 && g_stamps_r16 != nullptr)                                 \
-            g_stamps_r16[2 * ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) + (S)] =     \
-                __builtin_amdgcn_s_memrealtime();                                         \
-    } while (0)
-#else
-#define MLA_STAMP(S) ((void)0)
 #endif
 
 
@@ -192,11 +182,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
     const int rt = blockIdx.y;
     const int R = p.s_q * p.h_q;
 
-    MLA_STAMP(0);
+    MLA_STAMP_BEGIN();
     const int32_t *rec = meta + part * kPartInts;
     const int s0 = rec[0];
     if (s0 < 0) {
-        MLA_STAMP(1);
+        MLA_STAMP_END(g_stamps_r16);
         return;
     }
     const int t0 = rec[1], s1 = rec[2], t1 = rec[3], slot0 = rec[4];
@@ -212,6 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
         const int ks = seq == s0 ? t0 : 0;
         const int ke = seq == s1 ? t1 : n;
         if (ks >= ke) continue;   // empty sequence inside the part (uniform)
+        MLA_STAMP_SEGMENT();
         const int nsplit = split_off[seq + 1] - split_off[seq];
         const int slot = seq == s0 ? slot0 : split_off[seq];
 
@@ -238,6 +229,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
         const int c_end = (ke + kChunk - 1) / kChunk;
         const int mine = c_end - c_begin - wave;
         const int nc = mine > 0 ? (mine + kWaves - 1) / kWaves : 0;
+        MLA_STAMP_PHASE(0);
         if (nc > 0) {
             ChunkRegs ka, kb;
             int c = c_begin + wave;
@@ -257,6 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
             }
         }
 
+        MLA_STAMP_PHASE(1);
         // ---- merge the four wave states --------------------------------
         st.l += __shfl_xor(st.l, 16);
         st.l += __shfl_xor(st.l, 32);
@@ -327,10 +320,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
             if (wave == 0 && (lane & 3) == 0) p.lse_part[(int64_t)slot * R + orow] = lse_v;
         }
         __syncthreads();   // before the next segment reuses LDS
+        MLA_STAMP_PHASE(2);
     }
-    MLA_STAMP(1);
+    MLA_STAMP_END(g_stamps_r16);
 }
-#undef MLA_STAMP
 
 hipError_t launch_decode_r16(const DecodeParams &p, int num_parts, int row_tiles,
                              hipStream_t stream)

@@ -58,6 +58,7 @@
 // clobbered.
 #include "mla_device.h"
 #include "kernels.h"
+#include "stamps.h"
 #include "tile_layout.h"
 
 namespace mla {
@@ -73,23 +74,12 @@ constexpr float kWOriginSlack = 64.0f;   // log2 units
 constexpr int kPvAhead = 2;              // value fragments (pairs of reads) read ahead
 
 #if MLA_STAMPS
-// Instrumented build only (MLA_STAMPS=1, a separate library): each
-// workgroup's start and end in 100 MHz ticks, [workgroup][2] with workgroups
-// numbered in dispatch order (x fastest), into a buffer set by
-// mla_stamps_set; nothing is written while it is null.
+// Instrumented build only: the record buffer of stamps.h, or null.
 __device__ uint64_t *g_stamps_wide;
 hipError_t set_stamps_wide(uint64_t *buf)
 {
     return hipMemcpyToSymbol(HIP_SYMBOL(g_stamps_wide), &buf, sizeof(buf));
 }
-#define MLA_STAMP(S)                                                                      \
-    do {                                                                                  \
-        if (threadIdx.x == 0 && g_stamps_wide != nullptr)                                 \
-            g_stamps_wide[2 * ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) + (S)] =     \
-                __builtin_amdgcn_s_memrealtime();                                         \
-    } while (0)
-#else
-#define MLA_STAMP(S) ((void)0)
 #endif
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -555,11 +545,11 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
     const int rt = blockIdx.y;
     const int R = p.s_q * p.h_q;
 
-    MLA_STAMP(0);
+    MLA_STAMP_BEGIN();
     const int32_t *rec = meta + part * kPartInts;
     const int s0 = rec[0];
     if (s0 < 0) {
-        MLA_STAMP(1);
+        MLA_STAMP_END(g_stamps_wide);
         return;
     }
     const int t0 = rec[1], s1 = rec[2], t1 = rec[3], slot0 = rec[4];
@@ -588,6 +578,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
         const int ks = seq == s0 ? t0 : 0;
         const int ke = seq == s1 ? t1 : n;
         if (ks >= ke) continue;
+        MLA_STAMP_SEGMENT();
         const int nsplit = split_off[seq + 1] - split_off[seq];
         const int slot = seq == s0 ? slot0 : split_off[seq];
         const int32_t *bt_row = bt + (int64_t)seq * p.bt_stride;
@@ -670,6 +661,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
             bf16x8_t pp0 = {}, pp1 = {}, rp0 = {}, rp1 = {};
             bool low_any = false;         // some row of the wave outgrew its origin
             float mrun = -INFINITY;       // running maximum of the row's scores
+            MLA_STAMP_PHASE(0);
             for (int t = 0; t < ntiles; ++t) {
                 const int T = T0 + t;
                 // this wave's part of tile t has landed (tile t + 1 may still be
@@ -786,6 +778,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
             __syncthreads();
             const int again = redo;
             __syncthreads();
+            MLA_STAMP_PHASE(1);
             if (!again || attempt > 0) break;
             if (threadIdx.x == 0) redo = 0;
             m_hint = mrun;   // both halves of a row hold the same maximum
@@ -821,10 +814,10 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                 if (g == 0) p.lse_part[(int64_t)slot * R + row] = lse_v;
             }
         }
+        MLA_STAMP_PHASE(2);
     }
-    MLA_STAMP(1);
+    MLA_STAMP_END(g_stamps_wide);
 }
-#undef MLA_STAMP
 
 hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tiles,
                               hipStream_t stream)

@@ -89,15 +89,16 @@ struct MetaLayout {
     __host__ __device__ int64_t extra_max() const { return (B + P) / 4 + 1; }
 };
 
-hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int lead,
-                           int32_t *meta, hipStream_t stream);
+// seg_cost: the schedule's price of one sequence segment, in chunks, also
+// its lead; choose: pick the lead per call between 0 and seg_cost (see
+// metadata.hip)
+hipError_t launch_metadata(const int32_t *seqlens, int batch, int num_parts, int seg_cost,
+                           bool choose, int32_t *meta, hipStream_t stream);
 hipError_t launch_decode_r16(const DecodeParams &p, int num_parts, int row_tiles,
                              hipStream_t stream);
 // query rows per workgroup of the wide decode kernel (used when s_q*h_q is a
 // multiple of it)
 constexpr int kWideRows = 128;
-// schedule cost of starting a sequence, in chunks, for the kernel that
-// serves s_q * h_q rows (see metadata.hip)
 // The 128-row kernel serves multiples of 128 rows and, with a partly empty
 // last tile, any row count from 48 on (it streams the cache once per 128
 // rows instead of once per 16); the 16-row kernel serves 16 and 32 rows.
@@ -107,14 +108,11 @@ constexpr int decode_row_tiles(int rows)
 {
     return use_wide(rows) ? (rows + kWideRows - 1) / kWideRows : (rows + 15) / 16;
 }
-// Lead cost (chunks) of starting a sequence, chosen per row count by
-// interleaved timing of the leads 8, 16, 24, 32: 16 for the 16-row kernel
-// and for partly empty 128-row tiles (fewer rows per chunk of work), 8 at
-// 128 rows, 24 from two row tiles on (both tiles of a part pay the start).
-constexpr int schedule_lead(int rows)
-{
-    return !use_wide(rows) ? 16 : rows < kWideRows ? 16 : rows == kWideRows ? 8 : 24;
-}
+// The schedule's price of one sequence segment (query load, pipeline fill,
+// result write), in chunks, for the kernel serving s_q * h_q rows: 16 for
+// the 16-row kernel, 24 for the 128-row kernel (measured per-segment
+// overheads; metadata.hip picks each call's lead with it).
+constexpr int segment_cost(int rows) { return use_wide(rows) ? 24 : 16; }
 hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tiles,
                               hipStream_t stream);
 // `extra_wgs`: upper bound on the extra workgroups of heavily split sequences

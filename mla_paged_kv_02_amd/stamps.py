@@ -1,21 +1,25 @@
-"""When each decode workgroup starts and ends, from the instrumented build.
+"""When each decode workgroup starts and ends, and where its time goes, from
+the instrumented build.
 
     python -m mla_paged_kv_02_amd.build --stamps
     python -m mla_paged_kv_02_amd.stamps --config memory_bound --reps 20
 
 The instrumented library (libmla_paged_kv_stamps.so: the same sources built
-with MLA_STAMPS=1) makes every workgroup of the decode kernels write its
-start and end time (s_memrealtime, 100 MHz) to a buffer.  Workgroups are
-numbered in dispatch order, x fastest, and consecutive numbers go to the
-eight XCDs in turn, so number mod 8 is the XCD.  For each call the script
-measures times from the first start and prints, as one JSON line, medians
-over the calls of: the kernel span (last end), the median workgroup end,
-the tail (last end minus median end), the median workgroup duration, per
-XCD the median and last end, and the whole mla_decode call (decode and
-merge kernels) timed with HIP events on its stream.  As in the benchmark,
-consecutive calls read different copies of the cache (at least 1 GiB in
-all), so the last-level cache does not serve a call what the previous one
-read.
+with MLA_STAMPS=1) makes every workgroup of the decode kernels write a
+timing record (csrc/stamps.h): its start and end (s_memrealtime, 100 MHz)
+and the ticks it spent in segment set-up, in the key loop and in the merge
+and stores, with its segment count.  Workgroups are numbered in dispatch
+order, x fastest, and consecutive numbers go to the eight XCDs in turn, so
+number mod 8 is the XCD.  For each call the script measures times from the
+first start and prints, as one JSON line, medians over the calls of: the
+kernel span (last end), the median workgroup end, the tail (last end minus
+median end), the median workgroup duration, the median per workgroup of
+each phase and the mean segments per workgroup, per XCD the median and last
+end, and the whole mla_decode call (decode and merge kernels) timed with HIP
+events on its stream (host launch time included: each call is synchronized
+before the next).  As in the benchmark, consecutive calls read different
+copies of the cache (at least 1 GiB in all), so the last-level cache does
+not serve a call what the previous one read.
 """
 from __future__ import annotations
 
@@ -63,7 +67,8 @@ def main(argv=None) -> int:
     rows = x.s_q * x.h_q
     # an upper bound on the grid: parts x (16-row tiles), enough for either kernel
     wgs = parts * ((rows + 15) // 16)
-    stamps = torch.zeros(2 * wgs, dtype=torch.int64, device=dev)
+    words = 8                                            # kStampWords in csrc/stamps.h
+    stamps = torch.zeros(words * wgs, dtype=torch.int64, device=dev)
     _lib.check(lib.mla_stamps_set(stamps.data_ptr()), "mla_stamps_set")
     meta, parts = api.get_metadata(seqlens, x.s_q, x.h_q, parts)
     out = torch.empty((x.batch, x.s_q, x.h_q, 512), dtype=torch.bfloat16, device=dev)
@@ -71,7 +76,7 @@ def main(argv=None) -> int:
     ws = torch.empty(api.workspace_bytes(x.batch, x.s_q, x.h_q, parts), dtype=torch.uint8,
                      device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    spans, meds, tails, durs, per_xcd, calls = [], [], [], [], [], []
+    spans, meds, tails, durs, per_xcd, calls, phases, segs = [], [], [], [], [], [], [], []
     try:
         for i in range(args.reps + 2):
             stamps.zero_()
@@ -83,9 +88,11 @@ def main(argv=None) -> int:
             if i < 2:
                 continue                                 # warm-up calls
             calls.append(e0.elapsed_time(e1) * 1e3)
-            raw = stamps.cpu().numpy().reshape(-1, 2)
+            raw = stamps.cpu().numpy().reshape(-1, words)
             ids = np.nonzero(raw[:, 0] > 0)[0]                  # launched workgroups only
-            t = raw[ids].astype(np.float64) / 100.0             # 100 MHz ticks -> µs
+            t = raw[ids, :5].astype(np.float64) / 100.0         # 100 MHz ticks -> µs
+            phases.append(np.median(t[:, 2:5], axis=0))
+            segs.append(raw[ids, 5].mean())
             t0 = t[:, 0].min()
             start, end = t[:, 0] - t0, t[:, 1] - t0
             spans.append(end.max())
@@ -105,6 +112,10 @@ def main(argv=None) -> int:
         "median_end_us": round(float(np.median(meds)), 2),
         "tail_us": round(float(np.median(tails)), 2),
         "median_workgroup_us": round(float(np.median(durs)), 2),
+        "median_setup_us": round(float(np.median([v[0] for v in phases])), 2),
+        "median_loop_us": round(float(np.median([v[1] for v in phases])), 2),
+        "median_merge_us": round(float(np.median([v[2] for v in phases])), 2),
+        "segments_per_workgroup": round(float(np.median(segs)), 3),
         "xcd_median_end_us": [round(float(v), 2) for v in px[:, 0]],
         "xcd_last_end_us": [round(float(v), 2) for v in px[:, 1]],
     }))

@@ -25,12 +25,37 @@ def capped(seqlens):
     return np.clip(np.asarray(seqlens, dtype=np.int64), 0, MAX_SEQ_LEN)
 
 
-def lead_for(s_q, h_q):
-    """Cost of starting a sequence, in chunks, for s_q*h_q rows: 16 below 128
-    rows (the 16-row kernel, and partly empty 128-row tiles), 8 at exactly
-    128 rows, 24 above (two or more 128-row tiles)."""
+def is_wide(s_q, h_q):
+    """True when the 128-row kernel serves s_q * h_q rows (48 and more)."""
     r = s_q * h_q
-    return 16 if r < WIDE_ROWS else 8 if r == WIDE_ROWS else 24
+    return r % WIDE_ROWS == 0 or r >= 48
+
+
+def segment_cost_for(s_q, h_q):
+    """The schedule's price of one sequence segment, in chunks: 24 for the
+    128-row kernel, 16 for the 16-row kernel."""
+    return 24 if is_wide(s_q, h_q) else 16
+
+
+def pick_lead(seqlens, num_parts, seg_cost, candidates):
+    """Among the candidate leads, the one whose cuts have the smallest largest
+    part when every segment costs seg_cost chunks (segment_costs); ties go
+    to the candidate nearest seg_cost."""
+    def key(lead):
+        c = segment_costs(expected_metadata(seqlens, num_parts, lead), seqlens, num_parts,
+                          seg_cost)
+        return (int(c.max()) if len(c) else 0, abs(lead - seg_cost))
+    return min(candidates, key=key)
+
+
+def expected_schedule(seqlens, num_parts, s_q, h_q):
+    """The full metadata mla_get_metadata writes for these lengths and rows:
+    the 16-row kernel's schedule uses its segment cost as the lead; the
+    128-row kernel's takes whichever of 0 and its segment cost prices
+    lower."""
+    cost = segment_cost_for(s_q, h_q)
+    lead = pick_lead(seqlens, num_parts, cost, (0, cost)) if is_wide(s_q, h_q) else cost
+    return expected_metadata(seqlens, num_parts, lead)
 
 
 def expected_metadata(seqlens, num_parts, lead):

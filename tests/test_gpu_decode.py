@@ -36,7 +36,7 @@ def test_tiny_config():
 def test_memory_bound_config():
     x = gen.make_config("memory_bound")
     _, meta, parts = _check(x)
-    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
+    assert np.array_equal(meta, sc.expected_schedule(x.seqlens, parts, x.s_q, x.h_q))
 
 
 def test_skewed_config():
@@ -52,7 +52,7 @@ def test_compute_bound_config():
     """All 128 sequences of the compute-bound workload (256 rows each, causal)."""
     x = gen.make_config("compute_bound")
     _, meta, parts = _check(x)
-    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
+    assert np.array_equal(meta, sc.expected_schedule(x.seqlens, parts, x.s_q, x.h_q))
 
 
 @pytest.mark.parametrize("name", ["multi_token_4", "multi_token_8"])
@@ -87,7 +87,7 @@ def test_edge_lengths(s_q, h_q, causal):
 def test_forced_part_counts(num_parts):
     x = gen.make_decode([700, 3000, 65, 1, 4097], s_q=2, h_q=16, causal=True, seed=7)
     _, meta, parts = _check(x, num_parts=num_parts, what="parts=%d" % num_parts)
-    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
+    assert np.array_equal(meta, sc.expected_schedule(x.seqlens, parts, x.s_q, x.h_q))
 
 
 def test_page_permutation_is_bitwise_invariant():
@@ -122,7 +122,7 @@ def test_metadata_reused_across_calls():
         gu.compare(gu.dev_to_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl,
                    "layer %d" % layer)
     m = meta.cpu().numpy()
-    assert np.array_equal(m, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
+    assert np.array_equal(m, sc.expected_schedule(x.seqlens, parts, x.s_q, x.h_q))
 
 
 def test_repeat_runs_are_bitwise_identical():
@@ -188,7 +188,7 @@ def test_forced_part_counts_wide_rows(num_parts):
     fall inside 32-token tiles and inside pages."""
     x = gen.make_decode([700, 3000, 65, 1, 4097, 0, 33], s_q=1, h_q=128, causal=False, seed=31)
     _, meta, parts = _check(x, num_parts=num_parts, what="wide parts=%d" % num_parts)
-    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
+    assert np.array_equal(meta, sc.expected_schedule(x.seqlens, parts, x.s_q, x.h_q))
 
 
 @pytest.mark.parametrize("s_q,h_q,num_parts", [(4, 16, 1), (4, 16, 7), (4, 16, 300),
@@ -203,7 +203,7 @@ def test_forced_part_counts_several_row_tiles(s_q, h_q, num_parts):
                         seed=37 + s_q)
     _, meta, parts = _check(x, num_parts=num_parts,
                             what="row tiles s_q=%d h_q=%d parts=%d" % (s_q, h_q, num_parts))
-    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
+    assert np.array_equal(meta, sc.expected_schedule(x.seqlens, parts, x.s_q, x.h_q))
 
 
 def test_largest_batch():
@@ -273,7 +273,7 @@ def test_largest_row_count(num_parts):
     count (16), and forced ones that split sequences several ways."""
     x = gen.make_decode([0, 1, 17, 100, 700, 2049], s_q=16, h_q=128, causal=True, seed=77)
     _, meta, parts = _check(x, num_parts=num_parts, what="2048 rows parts=%s" % num_parts)
-    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
+    assert np.array_equal(meta, sc.expected_schedule(x.seqlens, parts, x.s_q, x.h_q))
 
 
 @pytest.mark.parametrize("s_q,h_q", [(2, 64), (4, 32), (8, 16), (2, 128)])
@@ -304,7 +304,7 @@ def test_two_level_merge_with_many_first_level_groups():
     so the second level loops over them."""
     x = gen.make_decode([70000, 100, 3], s_q=1, h_q=16, causal=False, seed=60)
     _, meta, parts = _check(x, num_parts=4096, what="4096 parts")
-    assert np.array_equal(meta, sc.expected_metadata(x.seqlens, parts, sc.lead_for(x.s_q, x.h_q)))
+    assert np.array_equal(meta, sc.expected_schedule(x.seqlens, parts, x.s_q, x.h_q))
     ns = meta[8 * parts + 1] - meta[8 * parts]
     assert ns > 64 * 16
 
@@ -383,11 +383,11 @@ def test_schedule_batch_and_part_counts(batch, num_parts, s_q, h_q):
     rng = np.random.default_rng(batch * 1000 + num_parts)
     lens = rng.integers(0, 3000, batch).astype(np.int32)
     lens[rng.random(batch) < 0.2] = 0
-    lead = sc.lead_for(s_q, h_q)
     for seqlens in (lens, np.zeros(batch, dtype=np.int32)):
         meta, parts = mla.get_metadata(torch.from_numpy(seqlens).cuda(), s_q, h_q, num_parts)
         torch.cuda.synchronize()
-        assert np.array_equal(meta.cpu().numpy(), sc.expected_metadata(seqlens, parts, lead))
+        assert np.array_equal(meta.cpu().numpy(),
+                              sc.expected_schedule(seqlens, parts, s_q, h_q))
 
 
 @pytest.mark.parametrize("h_q", [16, 128])

@@ -89,19 +89,35 @@ def test_best_max_cost_matches_enumeration(seqlens, parts, cost):
     assert sc.best_max_cost(seqlens, parts, cost) == _brute_best(seqlens, parts, cost)
 
 
+def test_pick_lead_by_hand():
+    """Two sequences of 40 chunks over 3 parts, 8 chunks a segment: the
+    largest part (chunks + 8 per segment) is 43 with lead 0 (cuts at units
+    26, 53), 40 with lead 8 (32, 64), 46 with lead 16, 48 with 24 and 32, so
+    the schedule takes lead 8."""
+    seqlens, parts = [640, 640], 3
+    want = {0: 43, 8: 40, 16: 46, 24: 48, 32: 48}
+    for lead, m in want.items():
+        c = sc.segment_costs(sc.expected_metadata(seqlens, parts, lead), seqlens, parts, 8)
+        assert int(c.max()) == m, lead
+    assert sc.pick_lead(seqlens, parts, 8, (0, 8, 16, 24, 32)) == 8
+    assert sc.pick_lead(seqlens, parts, 8, (0, 16)) == 0
+    # an all-empty batch prices every lead at 0: the one nearest the cost
+    assert sc.pick_lead([0, 0], 4, 24, (0, 24)) == 24
+
+
 @pytest.mark.parametrize("name", ["memory_bound", "compute_bound", "skewed", "full_step",
                                   "multi_token_4", "multi_token_8", "len_1k", "len_5k"])
 def test_cuts_near_best_partition(name):
-    """With the per-sequence lead as the cost of every segment, the unit cuts
-    land within 3% (or two chunks) of the best largest part over all
-    contiguous cuts into the same number of parts (at 256 compute units): a
-    better cut rule has little to gain on these workloads."""
+    """With the segment cost the schedule prices, its cuts land within 3%
+    (or two chunks) of the best largest part over all contiguous cuts into
+    the same number of parts (at 256 compute units): a better cut rule has
+    little to gain on these workloads."""
     seqlens, s_q, h_q, _ = gen.config_shape(name)
     rows = s_q * h_q
     tiles = (rows + 127) // 128 if rows >= 48 else (rows + 15) // 16
     parts = 256 // tiles
-    lead = sc.lead_for(s_q, h_q)
-    meta = sc.expected_metadata(seqlens, parts, lead)
-    got = int(sc.segment_costs(meta, seqlens, parts, lead).max())
-    best = sc.best_max_cost(seqlens, parts, lead)
+    cost = sc.segment_cost_for(s_q, h_q)
+    meta = sc.expected_schedule(seqlens, parts, s_q, h_q)
+    got = int(sc.segment_costs(meta, seqlens, parts, cost).max())
+    best = sc.best_max_cost(seqlens, parts, cost)
     assert best <= got <= best + max(0.03 * best, 2), (got, best)
