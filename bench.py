@@ -257,8 +257,11 @@ def source_digest():
 
 def decode_kernel(rows):
     """The decode kernel the library runs for s_q * h_q = rows: the 128-row
-    one for multiples of 128 and from 48 rows on, else the 16-row one."""
-    return "decode_wide_kernel" if rows % 128 == 0 or rows >= 48 else "decode_r16_kernel"
+    one for multiples of 128 and from 48 rows on, its shared-row 32-row
+    variant for 32 rows, else the 16-row one."""
+    if rows % 128 == 0 or rows >= 48:
+        return "decode_wide_kernel"
+    return "decode_wide32_kernel" if rows == 32 else "decode_r16_kernel"
 
 
 def measured_traffic(config, x):
@@ -280,6 +283,27 @@ def measured_traffic(config, x):
     if decode not in k or "combine_kernel" not in k:
         return None
     return int(sum(k[n]["fetch_bytes"] + k[n]["write_bytes"] for n in (decode, "combine_kernel")))
+
+
+def copy_reference(torch, dev, nbytes):
+    """A plain device copy that moves `nbytes` in all (half read, half
+    written), timed like a bmm stage (HIP events, median of 20): from one of
+    16 source buffers in turn, so the last-level cache holds none of them.
+    The yardstick for the absorbed-weight bmms, which move as many bytes."""
+    half = nbytes // 2
+    srcs = [torch.ones(half, dtype=torch.uint8, device=dev) for _ in range(16)]
+    dst = torch.empty(half, dtype=torch.uint8, device=dev)
+    times = []
+    for i in range(24):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(srcs[i % 16])
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 4:
+            times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    return {"ms": round(ms, 5), "bytes": 2 * half, "GB/s": round(2 * half / (ms / 1e3) / 1e9, 2)}
 
 
 def time_workload(config, args, torch, mla, gen, dev):
@@ -418,7 +442,8 @@ def time_workload(config, args, torch, mla, gen, dev):
             return d
         stages = {"metadata": stage(st_meta, 0, 0), "absorb_w_uk": stage(st_uk, b1, f1),
                   "decode": stage(st_decode, nbytes, flops), "absorb_w_uv": stage(st_uv, b2, f2),
-                  "end_to_end": stage(st_all, b1 + nbytes + b2, f1 + flops + f2)}
+                  "end_to_end": stage(st_all, b1 + nbytes + b2, f1 + flops + f2),
+                  "copy_reference": copy_reference(torch, dev, b1)}
         step_bytes, step_flops = b1 + nbytes + b2, f1 + flops + f2
     value = step_bytes / (ms_step / 1e3) / 1e9
     achieved = nbytes / (decode_ms / 1e3) / 1e9

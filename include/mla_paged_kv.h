@@ -67,7 +67,7 @@ int mla_device_cus(int device, int *cus);
  * into so that one workgroup per part and row tile fills the device once.
  * A row tile is 128 query rows when s_q * h_q >= 48 (the MFMA-dense
  * kernel; the last tile is partly empty unless s_q * h_q is a multiple of
- * 128), else 16 rows.  Pure host arithmetic. */
+ * 128), 32 rows when s_q * h_q = 32, else 16 rows.  Pure host arithmetic. */
 int mla_default_num_parts(int num_cus, int batch, int s_q, int h_q);
 
 /* int32 count of the metadata buffer for (batch, num_parts):
@@ -104,11 +104,11 @@ size_t mla_workspace_bytes(int batch, int s_q, int h_q, int num_parts);
  * part p < U takes the chunks whose units fall in [floor(p*TC/U),
  * floor((p+1)*TC/U)), chunk i of sequence b sitting at unit (units of the
  * sequences before b) + C + i.  A part whose range holds lead units only is
- * empty.  With R = s_q * h_q, let S = 16 when R is 16 or 32 (the 16-row
- * kernel) and S = 24 otherwise (the 128-row kernel): S prices one segment
- * (a part's run of one sequence) in chunks.  For 16 or 32 rows C = S; for
- * more, C is 0 or S, whichever gives the smaller largest part when every
- * part costs its chunks plus S per segment (ties: S).  Writes the metadata
+ * empty.  With R = s_q * h_q, let S = 16 when R is 16 or 32 and S = 24
+ * from 48 rows on: S prices one segment (a part's run of one sequence) in
+ * chunks.  For 16 or 32 rows C = S; for more, C is 0 or S, whichever gives
+ * the smaller largest part when every part costs its chunks plus S per
+ * segment (ties: S).  Writes the metadata
  * described above.  Compute once per decode step; it stays valid for every
  * layer while the lengths do not change.
  *   seqlens  [device] int32 [batch]; a negative length counts as 0 and one

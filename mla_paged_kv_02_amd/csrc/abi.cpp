@@ -138,6 +138,8 @@ int absorb(const uint16_t *x, int64_t x_stride_b, int64_t x_stride_h, const uint
 
 namespace mla {
 
+
+
 int set_error(int status, const char *fmt, ...)
 {
     va_list ap;
@@ -217,11 +219,12 @@ int decode_call(const uint16_t *q, const uint16_t *kv_cache, int64_t num_pages,
     p.out = out;
     p.lse = lse;
     // 128-row tiles (the last one possibly partly empty) from 48 rows on,
-    // else 16-row tiles
+    // one shared-row 32-row tile at 32 rows, else 16-row tiles
     const int row_tiles = mla::decode_row_tiles(rows);
-    const hipError_t e = mla::use_wide(rows)
-                             ? mla::launch_decode_wide(p, num_parts, row_tiles, st)
-                             : mla::launch_decode_r16(p, num_parts, row_tiles, st);
+    const hipError_t e =
+        mla::use_wide(rows)     ? mla::launch_decode_wide(p, num_parts, row_tiles, st)
+        : mla::use_wide32(rows) ? mla::launch_decode_wide32(p, num_parts, row_tiles, st)
+                                : mla::launch_decode_r16(p, num_parts, row_tiles, st);
     if (e != hipSuccess) return hip_status(e, "decode kernel launch");
 
     // heavily split sequences get the schedule's extra merge workgroups

@@ -473,12 +473,14 @@ __device__ __forceinline__ void pv_read(const int vb[2][2], int d, int kk, i16x4
         (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[1][d & 1] + off));
 }
 
-// O^T[512 dims][32 rows] += V^T P^T for one tile, each weight as two terms
-// (pf + rf): 64 MFMAs, V^T fragments of (dim block d, k-step kk) at
-// vb[read][d % 2] + 2048 kk + 4096 (d / 2) (keys 16 apart are two row groups
-// apart with the same swizzle)
-__device__ __forceinline__ void pv_tile(f32x16_t o[kDBlocks], const int vb[2][2],
-                                        bf16x8_t pf0, bf16x8_t pf1, bf16x8_t rf0, bf16x8_t rf1)
+// O^T[dims][32 rows] += V^T P^T for one tile, each weight as two terms
+// (pf + rf), over kBlocks dim blocks of 32: 4 kBlocks MFMAs, V^T fragments
+// of (dim block d, k-step kk) at vb[read][d % 2] + 2048 kk + 4096 (d / 2)
+// (keys 16 apart are two row groups apart with the same swizzle; a wave
+// that starts at a later dim block has that offset in vb)
+template <int kBlocks>
+__device__ __forceinline__ void pv_tile(f32x16_t o[kBlocks], const int vb[2][2], bf16x8_t pf0,
+                                        bf16x8_t pf1, bf16x8_t rf0, bf16x8_t rf1)
 {
     i16x4_t vlo[kPvAhead], vhi[kPvAhead];
 #pragma unroll
@@ -490,16 +492,16 @@ __device__ __forceinline__ void pv_tile(f32x16_t o[kDBlocks], const int vb[2][2]
             (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[1][d & 1] + off));
     }
 #pragma unroll
-    for (int j = 0; j < 2 * kDBlocks; ++j) {
-        const int d = j >> 1, kk = j & 1;
+    for (int j = 0; j < 2 * kBlocks; ++j) {
+        const int lb = j >> 1, kk = j & 1;
         const i16x4_t lo = vlo[j % kPvAhead], hi = vhi[j % kPvAhead];
         const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       kk ? pf1 : pf0, o[d], 0, 0, 0);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       kk ? rf1 : rf0, o[d], 0, 0, 0);
+        o[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                        kk ? pf1 : pf0, o[lb], 0, 0, 0);
+        o[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                        kk ? rf1 : rf0, o[lb], 0, 0, 0);
         const int nj = j + kPvAhead;
-        if (nj < 2 * kDBlocks) {
+        if (nj < 2 * kBlocks) {
             const int nd = nj >> 1, nkk = nj & 1, off = 2048 * nkk + 4096 * (nd >> 1);
             vlo[j % kPvAhead] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (i16x4_t __attribute__((address_space(3))) *)(uintptr_t)(vb[0][nd & 1] + off));
@@ -529,10 +531,21 @@ __device__ __forceinline__ float half_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
-    DecodeParams p, const int32_t *__restrict__ bt, const int32_t *__restrict__ seqlens,
-    const int32_t *__restrict__ meta)
+// kQuad = false: wave w owns query rows [32 w, 32 w + 32) of a 128-row tile
+// over all 512 value dims.  kQuad = true: a 32-row tile whose rows all four
+// waves share, wave w owning value dims [128 w, 128 w + 128): every wave runs
+// the same score chain and softmax (the same LDS tile, no extra HBM bytes),
+// each multiplies a quarter of the value dims, and no cross-wave merge is
+// needed.  That serves 32 query rows from one pass over the cache.
+template <bool kQuad>
+__device__ __forceinline__ void decode_wide_body(DecodeParams p, const int32_t *__restrict__ bt,
+                                                 const int32_t *__restrict__ seqlens,
+                                                 const int32_t *__restrict__ meta)
 {
+    constexpr int kTileRows = kQuad ? 32 : kWRows;          // query rows per workgroup
+    constexpr int kBlocks = kQuad ? kDBlocks / kWWaves : kDBlocks;   // dim blocks per wave
+    constexpr int kPvSteps = 2 * kBlocks;                   // value MFMA pairs per tile
+    constexpr int kSteps = kPvSteps > 20 ? kPvSteps : 20;   // softmax needs 20 slices
     __shared__ __attribute__((aligned(1024))) char tiles[kStages * kTileBytes];
     // set by any wave whose rows need the segment redone; read by all after a
     // barrier that follows every write, cleared after a second barrier
@@ -567,10 +580,15 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
     // DMA: this lane's tile row and its in-page offset without tile and group terms
     const int trow = 8 * wave + (lane >> 3);
     const int lane_off = dma_lane_offset(wave, lane);
-    const int row = rt * kWRows + 32 * wave + n32;
+    const int row0 = rt * kTileRows + (kQuad ? 0 : 32 * wave);   // the wave's first row
+    const int row = row0 + n32;
+    // the wave's first dim block, kept in a vector register: the kernel has
+    // no scalar register to spare for it
+    int d_base = kQuad ? kBlocks * wave : 0;
+    if constexpr (kQuad) asm volatile("" : "+v"(d_base));
     // a row count that is not a multiple of 128 leaves the last tile partly
     // empty: waves without rows only fetch their share of each tile
-    const bool has_rows = rt * kWRows + 32 * wave < R;   // uniform
+    const bool has_rows = row0 < R;   // uniform
     const bool row_ok = row < R;
 
     for (int seq = s0; seq <= s1; ++seq) {
@@ -612,7 +630,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
         bf16x8_t qf[kKSteps];
         float m_hint = -INFINITY;     // origin of the second pass (segment maximum)
         WideRow st;
-        f32x16_t o[kDBlocks];
+        f32x16_t o[kBlocks];
         for (int attempt = 0;; ++attempt) {
             if (pw_base != ks / kPage) window_at(ks / kPage);
             // start the first two tiles' DMA (and, once per segment, the Q^T loads)
@@ -630,7 +648,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
             }
             st = WideRow{m_hint, 0.f, 0.f};
 #pragma unroll
-            for (int d = 0; d < kDBlocks; ++d) o[d] = f32x16_t{};
+            for (int d = 0; d < kBlocks; ++d) o[d] = f32x16_t{};
 
             // fragment addresses: K of tile t (stage t % 4), V of tile t - 1
             int kb[4], vb[2][2];
@@ -652,7 +670,8 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
 #pragma unroll
                     for (int par = 0; par < 2; ++par)
                         vb[rd][par] = lds_addr + (kStages - 1) * kTileBytes +
-                                      tile_off(key, 4 * par + 2 * th + (tc >> 1)) + 8 * (tc & 1);
+                                      tile_off(key, 4 * par + 2 * th + (tc >> 1)) + 8 * (tc & 1) +
+                                      4096 * (d_base >> 1);   // d_base is even
                 }
             }
 
@@ -706,21 +725,22 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                     uint32_t pw[8], pr[8];
                     i16x4_t vlo[kPvAhead], vhi[kPvAhead];
 #pragma unroll
-                    for (int j = 0; j < kPvAhead; ++j) pv_read(vb, pv_block(j), pv_kstep(j), vlo[j], vhi[j]);
+                    for (int j = 0; j < kPvAhead; ++j)
+                        pv_read(vb, pv_block(j), pv_kstep(j), vlo[j], vhi[j]);
 #pragma unroll
-                    for (int j = 0; j < 2 * kDBlocks; ++j) {
-                        const int d = pv_block(j), kk = pv_kstep(j);
-                        {
+                    for (int j = 0; j < kSteps; ++j) {
+                        if (j < kPvSteps) {
+                            const int lb = pv_block(j), kk = pv_kstep(j);
                             const i16x4_t lo = vlo[j % kPvAhead], hi = vhi[j % kPvAhead];
                             const i16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                __builtin_bit_cast(bf16x8_t, a), kk ? pp1 : pp0, o[d], 0, 0, 0);
-                            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                __builtin_bit_cast(bf16x8_t, a), kk ? rp1 : rp0, o[d], 0, 0, 0);
+                            o[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(bf16x8_t, a), kk ? pp1 : pp0, o[lb], 0, 0, 0);
+                            o[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(bf16x8_t, a), kk ? rp1 : rp0, o[lb], 0, 0, 0);
+                            if (j + kPvAhead < kPvSteps)
+                                pv_read(vb, pv_block(j + kPvAhead), pv_kstep(j + kPvAhead),
+                                        vlo[j % kPvAhead], vhi[j % kPvAhead]);
                         }
-                        if (j + kPvAhead < 2 * kDBlocks)
-                            pv_read(vb, pv_block(j + kPvAhead), pv_kstep(j + kPvAhead),
-                                    vlo[j % kPvAhead], vhi[j % kPvAhead]);
                         __builtin_amdgcn_sched_barrier(0);
                         // ---- softmax slice j of tile t (lane: row n32, keys
                         //      8(r/4) + 4g + r%4) ----
@@ -771,7 +791,7 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                 for (int j = 0; j < 4; ++j) vb[j >> 1][j & 1] += vstep;
             }
             // the last tile's value product (its softmax ran in the last iteration)
-            if (has_rows) pv_tile(o, vb, pp0, pp1, rp0, rp1);
+            if (has_rows) pv_tile<kBlocks>(o, vb, pp0, pp1, rp0, rp1);
             if (low_any) redo = 1;
             // drain the DMA pipeline; every wave sees the same redo flag
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -784,16 +804,17 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
             m_hint = mrun;   // both halves of a row hold the same maximum
         }
 
-        // ---- epilogue: this wave's 32 rows, no cross-wave merge ----
+        // ---- epilogue: this wave's 32 rows (its dims of them with kQuad),
+        //      no cross-wave merge ----
         st.l = half_sum(st.l);
         st.lr = half_sum(st.lr);
         const float inv = st.lr > 0.f ? 1.f / st.lr : 0.f;
         const float lse_v = st.l > 0.f ? (st.m + fast_log2(st.l)) * kLn2 : -INFINITY;
         if (row_ok) {   // rows of a partial last tile are not written
             if (nsplit == 1) {
-                uint16_t *dst = p.out + ((int64_t)seq * R + row) * kDv + 4 * g;
+                uint16_t *dst = p.out + ((int64_t)seq * R + row) * kDv + 32 * d_base + 4 * g;
 #pragma unroll
-                for (int d = 0; d < kDBlocks; ++d)
+                for (int d = 0; d < kBlocks; ++d)
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
                         u32x2_t v;
@@ -801,17 +822,17 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
                         v[1] = pack_bf16x2(o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv);
                         *reinterpret_cast<u32x2_t *>(dst + 32 * d + 8 * q4) = v;
                     }
-                if (g == 0) p.lse[(int64_t)seq * R + row] = lse_v;
+                if (g == 0 && (!kQuad || d_base == 0)) p.lse[(int64_t)seq * R + row] = lse_v;
             } else {
-                float *dst = p.o_part + ((int64_t)slot * R + row) * kDv + 4 * g;
+                float *dst = p.o_part + ((int64_t)slot * R + row) * kDv + 32 * d_base + 4 * g;
 #pragma unroll
-                for (int d = 0; d < kDBlocks; ++d)
+                for (int d = 0; d < kBlocks; ++d)
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4)
                         *reinterpret_cast<f32x4_t *>(dst + 32 * d + 8 * q4) =
                             f32x4_t{o[d][4 * q4] * inv, o[d][4 * q4 + 1] * inv,
                                     o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv};
-                if (g == 0) p.lse_part[(int64_t)slot * R + row] = lse_v;
+                if (g == 0 && (!kQuad || d_base == 0)) p.lse_part[(int64_t)slot * R + row] = lse_v;
             }
         }
         MLA_STAMP_PHASE(2);
@@ -819,10 +840,34 @@ __global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
     MLA_STAMP_END(g_stamps_wide);
 }
 
+// The int tables are separate restrict arguments: with no aliasing store the
+// compiler can read them through the scalar cache (wave-uniform indices).
+__global__ __launch_bounds__(kWThreads, 1) void decode_wide_kernel(
+    DecodeParams p, const int32_t *__restrict__ bt, const int32_t *__restrict__ seqlens,
+    const int32_t *__restrict__ meta)
+{
+    decode_wide_body<false>(p, bt, seqlens, meta);
+}
+
+__global__ __launch_bounds__(kWThreads, 1) void decode_wide32_kernel(
+    DecodeParams p, const int32_t *__restrict__ bt, const int32_t *__restrict__ seqlens,
+    const int32_t *__restrict__ meta)
+{
+    decode_wide_body<true>(p, bt, seqlens, meta);
+}
+
 hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tiles,
                               hipStream_t stream)
 {
     hipLaunchKernelGGL(decode_wide_kernel, dim3(num_parts, row_tiles), dim3(kWThreads), 0,
+                       stream, p, p.block_table, p.seqlens, p.meta);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_wide32(const DecodeParams &p, int num_parts, int row_tiles,
+                                hipStream_t stream)
+{
+    hipLaunchKernelGGL(decode_wide32_kernel, dim3(num_parts, row_tiles), dim3(kWThreads), 0,
                        stream, p, p.block_table, p.seqlens, p.meta);
     return hipGetLastError();
 }

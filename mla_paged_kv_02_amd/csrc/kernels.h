@@ -104,9 +104,13 @@ constexpr int kWideRows = 128;
 // rows instead of once per 16); the 16-row kernel serves 16 and 32 rows.
 constexpr int kWideMinRows = 48;
 constexpr bool use_wide(int rows) { return rows % kWideRows == 0 || rows >= kWideMinRows; }
+// 32 rows run on the shared-row variant of the 128-row kernel (one pass over
+// the cache instead of two 16-row passes); 16 rows on the 16-row kernel.
+constexpr bool use_wide32(int rows) { return rows == 32; }
 constexpr int decode_row_tiles(int rows)
 {
-    return use_wide(rows) ? (rows + kWideRows - 1) / kWideRows : (rows + 15) / 16;
+    return use_wide(rows) ? (rows + kWideRows - 1) / kWideRows
+                          : use_wide32(rows) ? 1 : (rows + 15) / 16;
 }
 // The schedule's price of one sequence segment (query load, pipeline fill,
 // result write), in chunks, for the kernel serving s_q * h_q rows: 16 for
@@ -115,6 +119,8 @@ constexpr int decode_row_tiles(int rows)
 constexpr int segment_cost(int rows) { return use_wide(rows) ? 24 : 16; }
 hipError_t launch_decode_wide(const DecodeParams &p, int num_parts, int row_tiles,
                               hipStream_t stream);
+hipError_t launch_decode_wide32(const DecodeParams &p, int num_parts, int row_tiles,
+                                hipStream_t stream);
 // `extra_wgs`: upper bound on the extra workgroups of heavily split sequences
 hipError_t launch_combine(const CombineParams &p, int batch, int extra_wgs, hipStream_t stream);
 hipError_t launch_absorb(const AbsorbParams &p, int heads, hipStream_t stream);

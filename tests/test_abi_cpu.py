@@ -50,7 +50,8 @@ def test_sizes(lib):
     assert lib.mla_default_num_parts(256, 8, 1, 128) == 256     # one 128-row tile
     assert lib.mla_default_num_parts(256, 8, 3, 32) == 256      # 96 rows: one partial 128-row tile
     assert lib.mla_default_num_parts(256, 8, 5, 32) == 128      # 160 rows: two 128-row tiles
-    assert lib.mla_default_num_parts(256, 8, 2, 16) == 128      # 32 rows: two 16-row tiles
+    assert lib.mla_default_num_parts(256, 8, 2, 16) == 256      # 32 rows: one 32-row tile
+    assert lib.mla_default_num_parts(256, 8, 1, 16) == 256      # 16 rows: one 16-row tile
 
 
 def _decode(lib, **kw):

@@ -88,13 +88,15 @@ def test_more_than_one_gpu_is_refused():
 def test_decode_kernel_rule_matches_the_library():
     """The bench names (and looks up traffic for) the kernel the library
     dispatches.  The library's default part count is CUs / row tiles, and
-    the row tiles follow the kernel (128 rows for the wide one, 16 for the
-    other), so the part count tells which kernel the library picks."""
+    the row tiles follow the kernel (128 rows for the wide one, one tile for
+    its 32-row variant, 16 rows for the 16-row one), so the part count tells
+    which kernel the library picks."""
     b = _bench()
     from mla_paged_kv_02_amd import _lib
     lib = _lib.load()
     for s_q, h_q in ((1, 16), (1, 32), (3, 16), (1, 64), (4, 16), (1, 128), (2, 128), (16, 128)):
         rows = s_q * h_q
-        tiles = (rows + 127) // 128 if b.decode_kernel(rows) == "decode_wide_kernel" \
-            else (rows + 15) // 16
+        kern = b.decode_kernel(rows)
+        tiles = (rows + 127) // 128 if kern == "decode_wide_kernel" \
+            else 1 if kern == "decode_wide32_kernel" else (rows + 15) // 16
         assert lib.mla_default_num_parts(256, 1, s_q, h_q) == max(1, 256 // tiles), (s_q, h_q)

@@ -83,10 +83,11 @@ def test_edge_lengths(s_q, h_q, causal):
     _check(x, what="edge s_q=%d h_q=%d causal=%d" % (s_q, h_q, causal))
 
 
+@pytest.mark.parametrize("s_q", [1, 2])   # 16 rows: the 16-row kernel; 32: its 32-row variant
 @pytest.mark.parametrize("num_parts", [1, 2, 3, 7, 256, 1024])
-def test_forced_part_counts(num_parts):
-    x = gen.make_decode([700, 3000, 65, 1, 4097], s_q=2, h_q=16, causal=True, seed=7)
-    _, meta, parts = _check(x, num_parts=num_parts, what="parts=%d" % num_parts)
+def test_forced_part_counts(s_q, num_parts):
+    x = gen.make_decode([700, 3000, 65, 1, 4097], s_q=s_q, h_q=16, causal=True, seed=7)
+    _, meta, parts = _check(x, num_parts=num_parts, what="s_q=%d parts=%d" % (s_q, num_parts))
     assert np.array_equal(meta, sc.expected_schedule(x.seqlens, parts, x.s_q, x.h_q))
 
 
@@ -283,11 +284,12 @@ def test_causal_multi_query_wide_rows(s_q, h_q):
     _check(x, what="causal wide s_q=%d h_q=%d" % (s_q, h_q))
 
 
-@pytest.mark.parametrize("h_q", [16, 128])
+@pytest.mark.parametrize("h_q", [16, 32, 128])
 def test_scores_growing_after_first_key(h_q):
     """The first visible key scores far below a later one (2^240 apart in
     softmax weight): running-max rescaling (16-row kernel) and the exponent-
-    origin redo (128-row kernel) must both reach the oracle's result."""
+    origin redo (128-row kernel and its 32-row variant) must reach the
+    oracle's result."""
     x = gen.make_decode([300, 150, 2000], s_q=1, h_q=h_q, causal=False, seed=50)
     one, two = gen.f32_to_bf16_bits(np.float32(1.0)), gen.f32_to_bf16_bits(np.float32(2.0))
     x.q[:] = one
@@ -316,7 +318,7 @@ def _clamped_table(bt, num_pages, width):
     return np.concatenate([t[:, :width], np.repeat(t[:, width - 1:width], 8, axis=1)], axis=1)
 
 
-@pytest.mark.parametrize("h_q", [16, 128])
+@pytest.mark.parametrize("h_q", [16, 32, 128])
 def test_out_of_range_table_entries_read_inside_the_cache(h_q):
     """Entries past the cache, negative entries and lengths past the table's
     width stay inside the buffers: the result is the oracle's on the table
@@ -335,7 +337,7 @@ def test_out_of_range_table_entries_read_inside_the_cache(h_q):
                "clamped table h_q=%d" % h_q)
 
 
-@pytest.mark.parametrize("h_q", [16, 128])
+@pytest.mark.parametrize("h_q", [16, 32, 128])
 def test_lengths_above_the_cap_count_as_the_cap(h_q):
     """A one-column table over one page turns a length of n keys into n/64
     copies of the page's 64 rows; softmax over copies equals softmax over
@@ -390,7 +392,7 @@ def test_schedule_batch_and_part_counts(batch, num_parts, s_q, h_q):
                               sc.expected_schedule(seqlens, parts, s_q, h_q))
 
 
-@pytest.mark.parametrize("h_q", [16, 128])
+@pytest.mark.parametrize("h_q", [16, 32, 128])
 def test_all_sequences_empty(h_q):
     """A batch in which every sequence is empty: no part gets work, every row
     is out = 0 and lse = -inf."""

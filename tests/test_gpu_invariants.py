@@ -1,6 +1,7 @@
 """GPU invariants of paged MLA decode that hold exactly or in closed form, for
-both kernels (16-row tiles at h_q = 16, 128-row tiles at h_q = 128), with a
-causal two-token query and part boundaries inside sequences:
+each kernel (the 16-row one at s_q 1 x h_q 16, the 32-row variant at s_q 2 x
+h_q 16, the 128-row one at s_q 2 x h_q 128; causal, so the two-token queries
+see different key counts) with part boundaries inside sequences:
 
 * scaling the cache's 512 latent dims by 2^k and the query's latent dims by
   2^-k leaves every score bit for bit unchanged (bf16 x bf16 products are
@@ -20,10 +21,12 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 LENS = [700, 65, 2000, 1, 129]
+SHAPES = [(1, 16), (2, 16), (2, 128)]   # (s_q, h_q): 16, 32 and 256 rows
 
 
-def _inputs(h_q, seed):
-    return gen.make_decode(LENS, s_q=2, h_q=h_q, causal=True, seed=seed)
+def _inputs(shape, seed):
+    s_q, h_q = shape
+    return gen.make_decode(LENS, s_q=s_q, h_q=h_q, causal=True, seed=seed)
 
 
 def _scaled_bits(bits, k):
@@ -36,23 +39,23 @@ def _bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("h_q", [16, 128])
+@pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("k", [12, -12])
-def test_latent_rescaling_is_exact(h_q, k):
-    x = _inputs(h_q, seed=300 + h_q)
+def test_latent_rescaling_is_exact(shape, k):
+    x = _inputs(shape, seed=300 + shape[1])
     out0, lse0, _, _ = gu.run_decode(gu.DeviceInputs(x))
-    y = _inputs(h_q, seed=300 + h_q)
+    y = _inputs(shape, seed=300 + shape[1])
     y.kv[..., :512] = _scaled_bits(y.kv[..., :512], k)
     y.q[..., :512] = _scaled_bits(y.q[..., :512], -k)
     out1, lse1, _, _ = gu.run_decode(gu.DeviceInputs(y))
     want = _scaled_bits(_bits(out0), k)
-    assert np.array_equal(_bits(out1), want), "output not scaled bit for bit (h_q=%d, k=%d)" % (h_q, k)
+    assert np.array_equal(_bits(out1), want), "output not scaled bit for bit (%s, k=%d)" % (shape, k)
     assert np.array_equal(lse1.cpu().numpy().view(np.uint32), lse0.cpu().numpy().view(np.uint32))
 
 
-@pytest.mark.parametrize("h_q", [16, 128])
-def test_zero_query_weights_keys_equally(h_q):
-    x = _inputs(h_q, seed=310 + h_q)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_zero_query_weights_keys_equally(shape):
+    x = _inputs(shape, seed=310 + shape[1])
     x.q[:] = 0
     out, lse, _, _ = gu.run_decode(gu.DeviceInputs(x))
     got, lg = gu.dev_to_f64(out), lse.cpu().numpy().astype(np.float64)
@@ -75,9 +78,9 @@ def test_zero_query_weights_keys_equally(h_q):
             assert np.max(np.abs(l - np.log(vis))) <= 1e-5, (b, i)
 
 
-@pytest.mark.parametrize("h_q", [16, 128])
-def test_constant_values_give_that_value_both_kernels(h_q):
-    x = _inputs(h_q, seed=320 + h_q)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_constant_values_give_that_value_every_kernel(shape):
+    x = _inputs(shape, seed=320 + shape[1])
     v = gen.f32_to_bf16_bits(np.linspace(-3, 3, 512).astype(np.float32))
     for b, n in enumerate(x.seqlens):
         for j in range(int(n)):
