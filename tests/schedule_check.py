@@ -31,6 +31,15 @@ def is_wide(s_q, h_q):
     return r % WIDE_ROWS == 0 or r >= 48
 
 
+def row_tiles(s_q, h_q):
+    """Workgroups per part: 128-row tiles on the 128-row kernel, one on its
+    32-row variant, 16-row tiles on the 16-row kernel."""
+    r = s_q * h_q
+    if is_wide(s_q, h_q):
+        return -(-r // WIDE_ROWS)
+    return 1 if r == 32 else -(-r // 16)
+
+
 def segment_cost_for(s_q, h_q):
     """The schedule's price of one sequence segment, in chunks: 24 for the
     128-row kernel, 16 for the 16-row kernel."""

@@ -195,11 +195,11 @@ def test_forced_part_counts_wide_rows(num_parts):
 @pytest.mark.parametrize("s_q,h_q,num_parts", [(4, 16, 1), (4, 16, 7), (4, 16, 300),
                                               (3, 32, 3), (3, 32, 64), (5, 16, 11),
                                               (1, 32, 256), (7, 16, 5)])
-def test_forced_part_counts_several_row_tiles(s_q, h_q, num_parts):
-    """16-row tiles when s_q * h_q is above 16 but not a multiple of 128 (32,
-    64, 80, 96, 112 rows: two to seven row tiles per part) under several part
-    counts: parts that hold several sequence segments, splits inside chunks
-    and pages, causal rows."""
+def test_forced_part_counts_partial_row_tiles(s_q, h_q, num_parts):
+    """Row counts that fill no tile exactly -- 64, 80, 96 and 112 rows on
+    one partly used 128-row tile, 32 rows on the 32-row variant -- under
+    several part counts: parts that hold several sequence segments, splits
+    inside chunks and pages, causal rows."""
     x = gen.make_decode([700, 3000, 65, 1, 4097, 0, 33], s_q=s_q, h_q=h_q, causal=s_q > 1,
                         seed=37 + s_q)
     _, meta, parts = _check(x, num_parts=num_parts,

@@ -113,9 +113,7 @@ def test_cuts_near_best_partition(name):
     the same number of parts (at 256 compute units): a better cut rule has
     little to gain on these workloads."""
     seqlens, s_q, h_q, _ = gen.config_shape(name)
-    rows = s_q * h_q
-    tiles = (rows + 127) // 128 if rows >= 48 else (rows + 15) // 16
-    parts = 256 // tiles
+    parts = 256 // sc.row_tiles(s_q, h_q)
     cost = sc.segment_cost_for(s_q, h_q)
     meta = sc.expected_schedule(seqlens, parts, s_q, h_q)
     got = int(sc.segment_costs(meta, seqlens, parts, cost).max())
