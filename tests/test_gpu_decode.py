@@ -301,9 +301,10 @@ def test_scores_growing_after_first_key(h_q):
     _check(x, what="score growth h_q=%d" % h_q)
 
 
-def test_two_level_merge_with_many_first_level_groups():
-    """A sequence cut into ~4000 parts: more than 64 first-level merge groups,
-    so the second level loops over them."""
+def test_heavy_merge_over_thousands_of_splits():
+    """A sequence cut into ~4000 parts: each of its rows is merged in 16 dim
+    slices, and a slice's 32 lane groups cover 512 splits per round trip, so
+    every group loops over its splits in several rounds."""
     x = gen.make_decode([70000, 100, 3], s_q=1, h_q=16, causal=False, seed=60)
     _, meta, parts = _check(x, num_parts=4096, what="4096 parts")
     assert np.array_equal(meta, sc.expected_schedule(x.seqlens, parts, x.s_q, x.h_q))
