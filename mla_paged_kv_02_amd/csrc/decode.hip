@@ -236,12 +236,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
             load_chunk(ka, p, bt, seq, c, ke, r16, g);
             for (int it = 0;; it += 2) {
                 const int cn = c + kWaves;
-                // always issue the next loads (the last chunk again at the end)
-                load_chunk(kb, p, bt, seq, it + 1 < nc ? cn : c, ke, r16, g);
+                // always issue the next loads; past the wave's last chunk they
+                // fall outside the buffer range (zeros, no memory traffic)
+                load_chunk(kb, p, bt, seq, it + 1 < nc ? cn : c, it + 1 < nc ? ke : 0, r16, g);
                 __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the compute
                 process_chunk(ka, qs, o, st, c, limit, p.scale_log2, stage, r16, g);
                 if (it + 1 >= nc) break;
-                load_chunk(ka, p, bt, seq, it + 2 < nc ? cn + kWaves : cn, ke, r16, g);
+                load_chunk(ka, p, bt, seq, it + 2 < nc ? cn + kWaves : cn, it + 2 < nc ? ke : 0,
+                           r16, g);
                 __builtin_amdgcn_sched_barrier(0);
                 process_chunk(kb, qs, o, st, cn, limit, p.scale_log2, stage, r16, g);
                 if (it + 2 >= nc) break;
