@@ -268,9 +268,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
         }
         __syncthreads();
 
-        // wave w finishes dims [128w, 128w + 128) of all 16 rows
+        // wave w finishes dims [128w, 128w + 128) of all 16 rows: lane (row
+        // nr, c) the 8-dim runs 128w + 32j + 8c, j < 4, so the four lanes of a
+        // row store 64 (bf16) or 128 (fp32) contiguous bytes per instruction
         const int nr = lane >> 2;
-        const int d0 = 128 * wave + 32 * (lane & 3);
+        const int d0 = 128 * wave + 8 * (lane & 3);
         float mw[kWaves];
         float M = -INFINITY;
 #pragma unroll
@@ -291,7 +293,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
             const float *src = mo + (w * 16 + nr) * kOStride + d0;
 #pragma unroll
             for (int e = 0; e < 32; e += 4) {
-                const f32x4_t v = *reinterpret_cast<const f32x4_t *>(src + e);
+                // acc[e..e+3] = dims d0 + 32 (e / 8) + e % 8 ..
+                const f32x4_t v = *reinterpret_cast<const f32x4_t *>(src + 32 * (e >> 3) + (e & 7));
                 acc[e] += a * v[0];
                 acc[e + 1] += a * v[1];
                 acc[e + 2] += a * v[2];
@@ -310,14 +313,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
                 v[1] = pack_bf16x2(acc[e + 2] * inv, acc[e + 3] * inv);
                 v[2] = pack_bf16x2(acc[e + 4] * inv, acc[e + 5] * inv);
                 v[3] = pack_bf16x2(acc[e + 6] * inv, acc[e + 7] * inv);
-                *reinterpret_cast<u32x4_t *>(dst + e) = v;
+                *reinterpret_cast<u32x4_t *>(dst + 32 * (e >> 3)) = v;
             }
             if (wave == 0 && (lane & 3) == 0) p.lse[(int64_t)seq * R + orow] = lse_v;
         } else {
             float *dst = p.o_part + ((int64_t)slot * R + orow) * kDv + d0;
 #pragma unroll
             for (int e = 0; e < 32; e += 4)
-                *reinterpret_cast<f32x4_t *>(dst + e) =
+                *reinterpret_cast<f32x4_t *>(dst + 32 * (e >> 3) + (e & 7)) =
                     f32x4_t{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
             if (wave == 0 && (lane & 3) == 0) p.lse_part[(int64_t)slot * R + orow] = lse_v;
         }
