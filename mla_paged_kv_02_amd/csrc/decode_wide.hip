@@ -812,15 +812,24 @@ __device__ __forceinline__ void decode_wide_body(DecodeParams p, const int32_t *
         const float lse_v = st.l > 0.f ? (st.m + fast_log2(st.l)) * kLn2 : -INFINITY;
         if (row_ok) {   // rows of a partial last tile are not written
             if (nsplit == 1) {
-                uint16_t *dst = p.out + ((int64_t)seq * R + row) * kDv + 32 * d_base + 4 * g;
+                // lane (row, g) holds dims 8 q4 + 4g .. + 4 of each block; one
+                // swap of the halves per word leaves dims 16 h + 8g .. + 8 in
+                // lane (row, g), so each store writes 16 bytes instead of 8
+                uint16_t *dst = p.out + ((int64_t)seq * R + row) * kDv + 32 * d_base + 8 * g;
 #pragma unroll
                 for (int d = 0; d < kBlocks; ++d)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        u32x2_t v;
-                        v[0] = pack_bf16x2(o[d][4 * q4] * inv, o[d][4 * q4 + 1] * inv);
-                        v[1] = pack_bf16x2(o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv);
-                        *reinterpret_cast<u32x2_t *>(dst + 32 * d + 8 * q4) = v;
+                    for (int h = 0; h < 2; ++h) {
+                        // q4 = 2h: o[d][8h + 0..3], q4 = 2h + 1: o[d][8h + 4..7]
+                        const int b = 8 * h;
+                        const auto lo = __builtin_amdgcn_permlane32_swap(
+                            pack_bf16x2(o[d][b] * inv, o[d][b + 1] * inv),
+                            pack_bf16x2(o[d][b + 4] * inv, o[d][b + 5] * inv), false, false);
+                        const auto hi = __builtin_amdgcn_permlane32_swap(
+                            pack_bf16x2(o[d][b + 2] * inv, o[d][b + 3] * inv),
+                            pack_bf16x2(o[d][b + 6] * inv, o[d][b + 7] * inv), false, false);
+                        *reinterpret_cast<u32x4_t *>(dst + 32 * d + 16 * h) =
+                            u32x4_t{lo[0], hi[0], lo[1], hi[1]};
                     }
                 if (g == 0 && (!kQuad || d_base == 0)) p.lse[(int64_t)seq * R + row] = lse_v;
             } else {
