@@ -810,17 +810,27 @@ __device__ __forceinline__ void decode_wide_body(DecodeParams p, const int32_t *
         st.lr = half_sum(st.lr);
         const float inv = st.lr > 0.f ? 1.f / st.lr : 0.f;
         const float lse_v = st.l > 0.f ? (st.m + fast_log2(st.l)) * kLn2 : -INFINITY;
-        if (row_ok) {   // rows of a partial last tile are not written
+        // Result stores.  Lane (row n, g) holds dims 8 q4 + 4g .. + 4 of each
+        // 32-dim block.  Swapping words between lane halves (32 apart) and
+        // between 16-lane rows (16 apart) gathers four lanes per output row,
+        // so a store instruction writes 16 rows x 64 contiguous bytes instead
+        // of 32 rows x 16 or 32.  After the swaps lane l holds a piece of row
+        // (l & 15) (first register) or 16 + (l & 15) (second register) at
+        // column offset 8 pc + 4g (fp32) or 16 pc + 8g (bf16), pc = (l >> 4) & 1.
+        // Every lane takes part in the swaps; only the stores skip rows >= R.
+        if (has_rows) {
+            const int pc = (lane >> 4) & 1;
+            const int row_x = row0 + (lane & 15);
+            const bool ok_x = row_x < R, ok_y = row_x + 16 < R;
             if (nsplit == 1) {
-                // lane (row, g) holds dims 8 q4 + 4g .. + 4 of each block; one
-                // swap of the halves per word leaves dims 16 h + 8g .. + 8 in
-                // lane (row, g), so each store writes 16 bytes instead of 8
-                uint16_t *dst = p.out + ((int64_t)seq * R + row) * kDv + 32 * d_base + 8 * g;
+                uint16_t *dst = p.out + ((int64_t)seq * R + row_x) * kDv + 32 * d_base + 16 * pc + 8 * g;
 #pragma unroll
-                for (int d = 0; d < kBlocks; ++d)
+                for (int d = 0; d < kBlocks; ++d) {
+                    u32x4_t w[2];
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        // q4 = 2h: o[d][8h + 0..3], q4 = 2h + 1: o[d][8h + 4..7]
+                        // q4 = 2h: o[d][8h + 0..3], q4 = 2h + 1: o[d][8h + 4..7]; after
+                        // the half swap lane (n, g) holds dims 16 h + 8g .. + 8
                         const int b = 8 * h;
                         const auto lo = __builtin_amdgcn_permlane32_swap(
                             pack_bf16x2(o[d][b] * inv, o[d][b + 1] * inv),
@@ -828,20 +838,39 @@ __device__ __forceinline__ void decode_wide_body(DecodeParams p, const int32_t *
                         const auto hi = __builtin_amdgcn_permlane32_swap(
                             pack_bf16x2(o[d][b + 2] * inv, o[d][b + 3] * inv),
                             pack_bf16x2(o[d][b + 6] * inv, o[d][b + 7] * inv), false, false);
-                        *reinterpret_cast<u32x4_t *>(dst + 32 * d + 16 * h) =
-                            u32x4_t{lo[0], hi[0], lo[1], hi[1]};
+                        w[h] = u32x4_t{lo[0], hi[0], lo[1], hi[1]};
                     }
-                if (g == 0 && (!kQuad || d_base == 0)) p.lse[(int64_t)seq * R + row] = lse_v;
+                    u32x4_t x, y;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const auto sw = __builtin_amdgcn_permlane16_swap(w[0][k], w[1][k], false, false);
+                        x[k] = sw[0];
+                        y[k] = sw[1];
+                    }
+                    if (ok_x) *reinterpret_cast<u32x4_t *>(dst + 32 * d) = x;
+                    if (ok_y) *reinterpret_cast<u32x4_t *>(dst + 16 * kDv + 32 * d) = y;
+                }
+                if (row_ok && g == 0 && (!kQuad || d_base == 0)) p.lse[(int64_t)seq * R + row] = lse_v;
             } else {
-                float *dst = p.o_part + ((int64_t)slot * R + row) * kDv + 32 * d_base + 4 * g;
+                float *dst = p.o_part + ((int64_t)slot * R + row_x) * kDv + 32 * d_base + 8 * pc + 4 * g;
 #pragma unroll
                 for (int d = 0; d < kBlocks; ++d)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        *reinterpret_cast<f32x4_t *>(dst + 32 * d + 8 * q4) =
-                            f32x4_t{o[d][4 * q4] * inv, o[d][4 * q4 + 1] * inv,
-                                    o[d][4 * q4 + 2] * inv, o[d][4 * q4 + 3] * inv};
-                if (g == 0 && (!kQuad || d_base == 0)) p.lse_part[(int64_t)slot * R + row] = lse_v;
+                    for (int h = 0; h < 2; ++h) {
+                        const int b = 8 * h;   // q4 = 2h and 2h + 1
+                        f32x4_t x, y;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const auto sw = __builtin_amdgcn_permlane16_swap(
+                                __float_as_uint(o[d][b + k] * inv), __float_as_uint(o[d][b + 4 + k] * inv),
+                                false, false);
+                            x[k] = __uint_as_float(sw[0]);
+                            y[k] = __uint_as_float(sw[1]);
+                        }
+                        if (ok_x) *reinterpret_cast<f32x4_t *>(dst + 32 * d + 16 * h) = x;
+                        if (ok_y) *reinterpret_cast<f32x4_t *>(dst + 16 * kDv + 32 * d + 16 * h) = y;
+                    }
+                if (row_ok && g == 0 && (!kQuad || d_base == 0)) p.lse_part[(int64_t)slot * R + row] = lse_v;
             }
         }
         MLA_STAMP_PHASE(2);
