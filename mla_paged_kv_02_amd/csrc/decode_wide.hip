@@ -819,6 +819,11 @@ __device__ __forceinline__ void decode_wide_body(DecodeParams p, const int32_t *
         // column offset 8 pc + 4g (fp32) or 16 pc + 8g (bf16), pc = (l >> 4) & 1.
         // Every lane takes part in the swaps; only the stores skip rows >= R.
         if (has_rows) {
+            // lane < 32 writes its row's lse; derived here, not a lane mask
+            // held in scalar registers across the key loop
+            int ll = lane;
+            asm volatile("" : "+v"(ll));
+            const bool lse_ok = ll < 32 && row0 + ll < R && (!kQuad || d_base == 0);
             const int pc = (lane >> 4) & 1;
             const int row_x = row0 + (lane & 15);
             const bool ok_x = row_x < R, ok_y = row_x + 16 < R;
@@ -850,7 +855,7 @@ __device__ __forceinline__ void decode_wide_body(DecodeParams p, const int32_t *
                     if (ok_x) *reinterpret_cast<u32x4_t *>(dst + 32 * d) = x;
                     if (ok_y) *reinterpret_cast<u32x4_t *>(dst + 16 * kDv + 32 * d) = y;
                 }
-                if (row_ok && g == 0 && (!kQuad || d_base == 0)) p.lse[(int64_t)seq * R + row] = lse_v;
+                if (lse_ok) p.lse[(int64_t)seq * R + row] = lse_v;
             } else {
                 float *dst = p.o_part + ((int64_t)slot * R + row_x) * kDv + 32 * d_base + 8 * pc + 4 * g;
 #pragma unroll
@@ -870,7 +875,7 @@ __device__ __forceinline__ void decode_wide_body(DecodeParams p, const int32_t *
                         if (ok_x) *reinterpret_cast<f32x4_t *>(dst + 32 * d + 16 * h) = x;
                         if (ok_y) *reinterpret_cast<f32x4_t *>(dst + 16 * kDv + 32 * d + 16 * h) = y;
                     }
-                if (row_ok && g == 0 && (!kQuad || d_base == 0)) p.lse_part[(int64_t)slot * R + row] = lse_v;
+                if (lse_ok) p.lse_part[(int64_t)slot * R + row] = lse_v;
             }
         }
         MLA_STAMP_PHASE(2);

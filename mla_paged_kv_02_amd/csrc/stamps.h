@@ -24,15 +24,17 @@ constexpr int kStampWords = 8;
 // The state lives in LDS, kept by thread 0, so no register is held across
 // the kernel for it (the 128-row kernel has none to spare): the start, the
 // last mark (low 32 bits: unsigned differences are exact below 2^32 ticks,
-// 42 s), the three phase sums and the segment count.
+// 42 s), the three phase sums, the segment count and the record's index
+// (taken at the start, so the end needs no register for the grid size).
 #define MLA_STAMP_BEGIN()                                                                 \
-    __shared__ uint32_t stp_s[7];                                                         \
+    __shared__ uint32_t stp_s[8];                                                         \
     if (threadIdx.x == 0) {                                                               \
         const uint64_t stp_t = MLA_CLOCK();                                               \
         stp_s[0] = (uint32_t)stp_t;                                                       \
         stp_s[1] = (uint32_t)(stp_t >> 32);                                               \
         stp_s[2] = (uint32_t)stp_t;                                                       \
         stp_s[3] = stp_s[4] = stp_s[5] = stp_s[6] = 0;                                    \
+        stp_s[7] = blockIdx.y * gridDim.x + blockIdx.x;                                   \
     }
 #define MLA_STAMP_SEGMENT()                                                               \
     do {                                                                                  \
@@ -52,8 +54,7 @@ constexpr int kStampWords = 8;
 #define MLA_STAMP_END(BUF)                                                                \
     do {                                                                                  \
         if (threadIdx.x == 0 && (BUF) != nullptr) {                                       \
-            uint64_t *stp_r =                                                             \
-                (BUF) + kStampWords * ((int64_t)blockIdx.y * gridDim.x + blockIdx.x);     \
+            uint64_t *stp_r = (BUF) + kStampWords * (int64_t)stp_s[7];                    \
             stp_r[0] = (uint64_t)stp_s[0] | ((uint64_t)stp_s[1] << 32);                   \
             stp_r[1] = MLA_CLOCK();                                                       \
             stp_r[2] = stp_s[3];                                                          \
