@@ -48,21 +48,23 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// A lane's 8 dims of a row: acc[0..3] = dims 4 lane .. + 3 and acc[4..7] =
+// dims 256 + 4 lane .. + 3, so each load or store instruction of a wave
+// covers one contiguous half row.
+constexpr int kHalfDv = kDv / 2;
+
 __device__ __forceinline__ void store_row(const CombineParams &p, int b, int row, int lane,
                                           const float acc[8], float lse_v)
 {
-    uint16_t *dst = p.out + ((int64_t)b * p.rows + row) * kDv + 8 * lane;
-    u32x4_t v;
-    v[0] = pack_bf16x2(acc[0], acc[1]);
-    v[1] = pack_bf16x2(acc[2], acc[3]);
-    v[2] = pack_bf16x2(acc[4], acc[5]);
-    v[3] = pack_bf16x2(acc[6], acc[7]);
-    *reinterpret_cast<u32x4_t *>(dst) = v;
+    uint16_t *dst = p.out + ((int64_t)b * p.rows + row) * kDv + 4 * lane;
+    *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *reinterpret_cast<u32x2_t *>(dst + kHalfDv) =
+        u32x2_t{pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
     if (lane == 0) p.lse[(int64_t)b * p.rows + row] = lse_v;
 }
 
 // acc += sum over this wave's splits s = s_begin, s_begin + stride, ... < ns
-// of w(s) * o_part[s][row][8 lane .. 8 lane + 7], up to 8 loads in flight
+// of w(s) * o_part[s][row][the lane's 8 dims], up to 8 loads in flight
 template <typename W>
 __device__ __forceinline__ void accumulate(const float *o_row, int64_t split_stride, int s_begin,
                                            int stride, int ns, int lane, W weight, float acc[8])
@@ -77,9 +79,9 @@ __device__ __forceinline__ void accumulate(const float *o_row, int64_t split_str
             a[u] = c[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             if (s < ns) {
                 w[u] = weight(s);            // 0 for an empty split
-                const float *src = o_row + s * split_stride + 8 * lane;
+                const float *src = o_row + s * split_stride + 4 * lane;
                 a[u] = *reinterpret_cast<const f32x4_t *>(src);
-                c[u] = *reinterpret_cast<const f32x4_t *>(src + 4);
+                c[u] = *reinterpret_cast<const f32x4_t *>(src + kHalfDv);
             }
         }
 #pragma unroll
@@ -108,9 +110,9 @@ __device__ __forceinline__ void merge_row_wave(const float *o_row, int64_t slot_
         for (int u = 0; u < kCombineInflight; ++u) {
             a[u] = c[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             if (u < count) {   // uniform
-                const float *src = o_row + u * slot_stride + 8 * lane;
+                const float *src = o_row + u * slot_stride + 4 * lane;
                 a[u] = *reinterpret_cast<const f32x4_t *>(src);
-                c[u] = *reinterpret_cast<const f32x4_t *>(src + 4);
+                c[u] = *reinterpret_cast<const f32x4_t *>(src + kHalfDv);
             }
         }
         const float ls = lane < count ? lse_col[(int64_t)lane * lse_stride] : -INFINITY;
