@@ -50,6 +50,10 @@
 //    as its origin, which no score can exceed: at most two passes.  Real
 //    attention scores never grow like that after the first key, so the redo
 //    is a correctness path.
+//  * Results go out as bf16 rows (a sequence the schedule did not cut) or
+//    fp32 partials with their lse.  Lane swaps 32 and 16 lanes apart first
+//    gather four lanes per output row, so a store instruction writes 16 rows
+//    x 64 contiguous bytes rather than 32 rows x 16 or 32.
 //
 // The QK^T chains and the DMA are inline assembly (below); everything they
 // touch is passed as operands, M0 -- which the LDS DMA takes its
