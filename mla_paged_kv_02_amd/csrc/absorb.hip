@@ -14,14 +14,15 @@
 // 128 x 512), so every thread issues the loads of G 32-row slabs of k at
 // once -- G = 4 for K = 128, 16 for K = 512, 8 otherwise -- and the
 // workgroup pays one memory round trip per G slabs instead of one per slab.
-// The accumulator layout puts 4 consecutive output columns in each lane, so
-// stores are 8 bytes.  Consecutive workgroup numbers go to the eight XCDs in
-// turn, and each XCD has its own L2: the grid is numbered so that all tiles
-// of a head share an XCD (number L -> XCD L % 8, head L % 8 + 8 ((L / 8) /
-// tiles per head)), which keeps a head's x rows and W slabs in one L2
-// instead of fetching them from HBM once per XCD.  With fewer than 8 heads
-// (one head with the heads folded into K is a plain matmul) the tiles are
-// numbered in order instead, so that all XCDs share the work.
+// The accumulator layout puts 4 consecutive output columns in each lane;
+// two lane swaps regroup them so that stores are 16 bytes.  Consecutive
+// workgroup numbers go to the eight XCDs in turn, and each XCD has its own
+// L2: the grid is numbered so that all tiles of a head share an XCD (number
+// L -> XCD L % 8, head L % 8 + 8 ((L / 8) / tiles per head)), which keeps a
+// head's x rows and W slabs in one L2 instead of fetching them from HBM once
+// per XCD.  With fewer than 8 heads (one head with the heads folded into K
+// is a plain matmul) the tiles are numbered in order instead, so that all
+// XCDs share the work.
 //
 // The same PR stores the weights in fp8 and decompresses them to 16-bit
 // floats for the bmm.  With fp8 weights (OCP E4M3 codes, one fp32 scale per
@@ -221,16 +222,27 @@ __global__ __launch_bounds__(kAbsThreads, 2) void absorb_kernel(AbsorbParams p, 
             }
         }
         if (grp == ngroups - 1) {
-            // the item is complete: its 64 x 64 tile goes out, 8 bytes per lane and block
+            // the item is complete: its 64 x 64 tile goes out.  Lane (r16, g)
+            // holds columns 16 mb + 4g .. + 4 of row r16; a swap 32 lanes apart
+            // and one 16 lanes apart (all four lanes of a row take part) leave
+            // lane (r16, g) columns 32 i + 8g .. + 8 in pair i, so each store
+            // writes 16 bytes and a row's four lanes 64 contiguous bytes
             const int brow = cur.m0 + wave * 16 + r16;
             if (brow < p.batch) {
                 uint16_t *yrow = p.y + (int64_t)brow * p.y_sb + (int64_t)cur.h * p.y_sh + cur.n0;
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    u32x2_t v;
-                    v[0] = pack_bf16x2(acc[mb][0], acc[mb][1]);
-                    v[1] = pack_bf16x2(acc[mb][2], acc[mb][3]);
-                    *reinterpret_cast<u32x2_t *>(yrow + 16 * mb + 4 * g) = v;
+                for (int i = 0; i < 2; ++i) {
+                    uint32_t x[2], z[2];
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const auto a = __builtin_amdgcn_permlane32_swap(
+                            pack_bf16x2(acc[2 * i][2 * k], acc[2 * i][2 * k + 1]),
+                            pack_bf16x2(acc[2 * i + 1][2 * k], acc[2 * i + 1][2 * k + 1]), false, false);
+                        const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[1], false, false);
+                        x[k] = b[0];
+                        z[k] = b[1];
+                    }
+                    *reinterpret_cast<u32x4_t *>(yrow + 32 * i + 8 * g) = u32x4_t{x[0], x[1], z[0], z[1]};
                 }
             }
 #pragma unroll
