@@ -150,12 +150,13 @@ def test_constant_values_give_that_value():
     assert np.max(np.abs(got - want)) <= 2.0 ** -7 * 2
 
 
-@pytest.mark.parametrize("n_parts", [4, 12, 40, 100])
+@pytest.mark.parametrize("n_parts", [1, 4, 8, 9, 12, 32, 33, 40, 64, 65, 100])
 def test_combine_entry_point(n_parts):
     """mla_combine on oracle partials over random key splits equals the
     unsplit oracle result: up to 8 splits (one round trip), 9..32 (lse first,
     rows eight at a time), more than 32 (the one-level merge with four waves
-    per row that the read-only entry point uses).  Random cut points leave
+    per row that the read-only entry point uses), with the counts on both
+    sides of each boundary.  Random cut points leave
     empty splits (lse -inf, weight 0), and the causal length-1 sequence has
     a row with no visible key at all."""
     x = gen.make_decode([300, 65, 1, 129], s_q=2, h_q=16, causal=True, seed=12)
@@ -310,6 +311,24 @@ def test_heavy_merge_over_thousands_of_splits():
     assert np.array_equal(meta, sc.expected_schedule(x.seqlens, parts, x.s_q, x.h_q))
     ns = meta[8 * parts + 1] - meta[8 * parts]
     assert ns > 64 * 16
+
+
+@pytest.mark.parametrize("h_q,target,num_parts", [
+    (16, 33, 39), (16, 63, 75), (16, 64, 77), (16, 127, 153), (16, 128, 154), (16, 255, 307),
+    (16, 256, 308), (128, 33, 41), (128, 64, 81), (128, 128, 162), (128, 256, 324)])
+def test_heavy_merge_slice_boundaries(h_q, target, num_parts):
+    """A long sequence among short ones cut into exactly `target` parts (the
+    part count chosen so, checked against the schedule): the decode call's
+    merge of a heavy sequence at each boundary of its dim-slice count (2
+    slices from 33 splits, 4 from 64, 8 from 128, 16 from 256; 63, 127 and
+    255 splits the last counts below), on both kernels."""
+    lens = [8192, 100, 37, 0, 500]
+    x = gen.make_decode(lens, s_q=1, h_q=h_q, causal=False, seed=90 + target)
+    _, meta, parts = _check(x, num_parts=num_parts,
+                            what="heavy merge h_q=%d splits=%d" % (h_q, target))
+    assert parts == num_parts
+    assert meta[8 * parts + 1] - meta[8 * parts] == target
+    assert np.array_equal(meta, sc.expected_schedule(x.seqlens, parts, x.s_q, x.h_q))
 
 
 def _clamped_table(bt, num_pages, width):
