@@ -165,6 +165,7 @@ __device__ __forceinline__ int part_cost(int part, int lead, int tc, int used, b
 // The leads the schedule tries when it chooses (see mla_get_metadata in the
 // public header): 0 and the segment cost.
 constexpr int kLeadCands = 2;
+static_assert(kMetaThreads % (64 * kLeadCands) == 0, "each candidate gets whole waves");
 
 __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *seqlens, int batch,
                                                                int num_parts, int seg_cost,
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *s
     __shared__ int splits[kMetaMaxBatch + 1];        // partial-slot offsets
     __shared__ unsigned char tail[kMetaMaxBatch];    // tokens in a sequence's last chunk
     __shared__ int scratch[3][2 * kMetaThreads / 64];   // one per scan: no reuse race
-    __shared__ int lead_max[kMetaThreads / 64][kLeadCands];
+    __shared__ int lead_max[kMetaThreads / 64];         // per wave: its candidate's largest part
     const int t = threadIdx.x;
     const int per = (batch + kMetaThreads - 1) / kMetaThreads;
     const int b0 = min(batch, t * per);
@@ -211,28 +212,24 @@ __global__ __launch_bounds__(kMetaThreads) void metadata_kernel(const int32_t *s
     // seg_cost chunks (ties: seg_cost)
     int lead = seg_cost;
     if (choose) {
-        int mx[kLeadCands];
-#pragma unroll 1
-        for (int i = 0; i < kLeadCands; ++i) {
-            const int ld = i == 0 ? 0 : seg_cost;
-            const int tci = total + ld * total_ne;
-            const int usedi = min(num_parts, tci);
-            const bool smalli = (int64_t)(tci + 1) * usedi < 0x7FFFFFFF;
-            int m = 0;
-            for (int part = t; part < usedi; part += kMetaThreads)
-                m = max(m, part_cost(part, ld, tci, usedi, smalli, prefix, nepre, batch, seg_cost));
+        // the two candidates are priced at once, each by half of the threads
+        constexpr int kHalf = kMetaThreads / kLeadCands;
+        const int i = t / kHalf;   // wave-uniform
+        const int ld = i == 0 ? 0 : seg_cost;
+        const int tci = total + ld * total_ne;
+        const int usedi = min(num_parts, tci);
+        const bool smalli = (int64_t)(tci + 1) * usedi < 0x7FFFFFFF;
+        int m = 0;
+        for (int part = t % kHalf; part < usedi; part += kHalf)
+            m = max(m, part_cost(part, ld, tci, usedi, smalli, prefix, nepre, batch, seg_cost));
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) m = max(m, __shfl_xor(m, off));
-            mx[i] = m;
-        }
-        if ((t & 63) == 0)
-#pragma unroll
-            for (int i = 0; i < kLeadCands; ++i) lead_max[t >> 6][i] = mx[i];
+        for (int off = 32; off > 0; off >>= 1) m = max(m, __shfl_xor(m, off));
+        if ((t & 63) == 0) lead_max[t >> 6] = m;
         __syncthreads();
         int m0 = 0, m1 = 0;
         for (int w = 0; w < kMetaThreads / 64; ++w) {
-            m0 = max(m0, lead_max[w][0]);
-            m1 = max(m1, lead_max[w][1]);
+            if (w < kHalf / 64) m0 = max(m0, lead_max[w]);
+            else m1 = max(m1, lead_max[w]);
         }
         if (m0 < m1) lead = 0;
     }
