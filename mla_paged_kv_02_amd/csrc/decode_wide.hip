@@ -59,7 +59,9 @@
 // touch is passed as operands, M0 -- which the LDS DMA takes its
 // destination from -- is set inside each block before use (no other code in
 // this kernel uses M0), and the blocks that add scalar offsets declare SCC
-// clobbered.
+// clobbered.  The cache DMA is marked non-temporal (nt): each cache row is
+// read once per row tile, and streaming it past the caches leaves them to
+// the split partials the merge reads back right after the call.
 #include "mla_device.h"
 #include "kernels.h"
 #include "stamps.h"
@@ -119,39 +121,39 @@ __device__ __forceinline__ void dma_issue(const TileDma &a)
     asm volatile(
         "s_mov_b32 m0, %4\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %2, %1, %3 offen lds\n"
+        "buffer_load_dwordx4 %2, %1, %3 offen nt lds\n"
         "s_add_u32 m0, %4, 4096\n"
         "s_add_u32 %0, %3, 128\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen nt lds\n"
         "s_add_u32 m0, %4, 8192\n"
         "s_add_u32 %0, %3, 256\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen nt lds\n"
         "s_add_u32 m0, %4, 12288\n"
         "s_add_u32 %0, %3, 384\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen nt lds\n"
         "s_add_u32 m0, %4, 16384\n"
         "s_add_u32 %0, %3, 512\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen nt lds\n"
         "s_add_u32 m0, %4, 20480\n"
         "s_add_u32 %0, %3, 640\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen nt lds\n"
         "s_add_u32 m0, %4, 24576\n"
         "s_add_u32 %0, %3, 768\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen nt lds\n"
         "s_add_u32 m0, %4, 28672\n"
         "s_add_u32 %0, %3, 896\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen nt lds\n"
         "s_add_u32 m0, %4, 32768\n"
         "s_add_u32 %0, %3, 1024\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %2, %1, %0 offen lds\n"
+        "buffer_load_dwordx4 %2, %1, %0 offen nt lds\n"
         : "=&s"(tmp)
         : "s"(a.rsrc), "v"(a.voff), "s"(a.soff), "s"(a.m0)
         : "memory", "scc");
@@ -316,7 +318,7 @@ __device__ __forceinline__ void qk_tile_dma(f32x16_t &s, const int kb[4],
         "ds_read_b128 %2, %7 offset:4096\n"
         "s_mov_b32 m0, %49\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %47, %46, %48 offen lds\n"
+        "buffer_load_dwordx4 %47, %46, %48 offen nt lds\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %12, %0\n"
         "ds_read_b128 %3, %8 offset:4096\n"
@@ -332,7 +334,7 @@ __device__ __forceinline__ void qk_tile_dma(f32x16_t &s, const int kb[4],
         "s_add_u32 m0, %49, 4096\n"
         "s_add_u32 %5, %48, 128\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen nt lds\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %16, %0\n"
         "ds_read_b128 %3, %8 offset:8192\n"
@@ -348,7 +350,7 @@ __device__ __forceinline__ void qk_tile_dma(f32x16_t &s, const int kb[4],
         "s_add_u32 m0, %49, 8192\n"
         "s_add_u32 %5, %48, 256\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen nt lds\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %20, %0\n"
         "ds_read_b128 %3, %8 offset:12288\n"
@@ -364,7 +366,7 @@ __device__ __forceinline__ void qk_tile_dma(f32x16_t &s, const int kb[4],
         "s_add_u32 m0, %49, 12288\n"
         "s_add_u32 %5, %48, 384\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen nt lds\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %24, %0\n"
         "ds_read_b128 %3, %8 offset:16384\n"
@@ -380,7 +382,7 @@ __device__ __forceinline__ void qk_tile_dma(f32x16_t &s, const int kb[4],
         "s_add_u32 m0, %49, 16384\n"
         "s_add_u32 %5, %48, 512\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen nt lds\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %28, %0\n"
         "ds_read_b128 %3, %8 offset:20480\n"
@@ -396,7 +398,7 @@ __device__ __forceinline__ void qk_tile_dma(f32x16_t &s, const int kb[4],
         "s_add_u32 m0, %49, 20480\n"
         "s_add_u32 %5, %48, 640\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen nt lds\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %32, %0\n"
         "ds_read_b128 %3, %8 offset:24576\n"
@@ -412,7 +414,7 @@ __device__ __forceinline__ void qk_tile_dma(f32x16_t &s, const int kb[4],
         "s_add_u32 m0, %49, 24576\n"
         "s_add_u32 %5, %48, 768\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen nt lds\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %36, %0\n"
         "ds_read_b128 %3, %8 offset:28672\n"
@@ -428,7 +430,7 @@ __device__ __forceinline__ void qk_tile_dma(f32x16_t &s, const int kb[4],
         "s_add_u32 m0, %49, 28672\n"
         "s_add_u32 %5, %48, 896\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen nt lds\n"
         "s_waitcnt lgkmcnt(3)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %40, %0\n"
         "ds_read_b128 %3, %8 offset:32768\n"
@@ -442,7 +444,7 @@ __device__ __forceinline__ void qk_tile_dma(f32x16_t &s, const int kb[4],
         "s_add_u32 m0, %49, 32768\n"
         "s_add_u32 %5, %48, 1024\n"
         "s_nop 0\n"
-        "buffer_load_dwordx4 %47, %46, %5 offen lds\n"
+        "buffer_load_dwordx4 %47, %46, %5 offen nt lds\n"
         "s_waitcnt lgkmcnt(1)\n"
         "v_mfma_f32_32x32x16_bf16 %0, %3, %44, %0\n"
         "s_waitcnt lgkmcnt(0)\n"
