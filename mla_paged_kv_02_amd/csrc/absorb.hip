@@ -149,13 +149,15 @@ __global__ __launch_bounds__(kAbsThreads, 2) void absorb_kernel(AbsorbParams p, 
 #pragma unroll
         for (int s = 0; s < G; ++s) {
             const int k0 = kg + min(s, ns - 1) * kAbsKSlab;
+            // the weights are read once per call: non-temporal, so that the
+            // caches keep the x rows the head's other column tiles re-read
             if (kFp8) {
-                r.wq[s] = *reinterpret_cast<const u32x2_t *>(w8h + (int64_t)(k0 + srow) * p.N +
-                                                             it.n0 + scol);
+                r.wq[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(
+                    w8h + (int64_t)(k0 + srow) * p.N + it.n0 + scol));
                 r.wsc[s] = sch[(k0 / kFp8Block) * nblocks];
             } else {
-                r.wv[s] = *reinterpret_cast<const u32x4_t *>(wh + (int64_t)(k0 + srow) * p.N +
-                                                             it.n0 + scol);
+                r.wv[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(
+                    wh + (int64_t)(k0 + srow) * p.N + it.n0 + scol));
             }
             r.xv[s] = *reinterpret_cast<const u32x4_t *>(xrow + k0 + 8 * g);
         }
