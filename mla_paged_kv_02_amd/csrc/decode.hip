@@ -206,12 +206,37 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
         const int nsplit = split_off[seq + 1] - split_off[seq];
         const int slot = seq == s0 ? slot0 : split_off[seq];
 
-        // the tile's 16 query rows -> LDS (16 B per thread and pass)
+        const int c_begin = ks / kChunk;
+        const int c_end = (ke + kChunk - 1) / kChunk;
+        const int mine = c_end - c_begin - wave;
+        const int nc = mine > 0 ? (mine + kWaves - 1) / kWaves : 0;
+        int c = c_begin + wave;
+
+        // the tile's 16 query rows -> LDS (16 B per thread and pass).  The
+        // wave's first chunk loads go out between the query loads and their
+        // LDS stores, so the two memory round trips overlap; they are issued
+        // even when the wave has no chunk (then all outside the buffer range)
+        // so that the wait before the stores counts the same loads on every path.
         const uint16_t *qtile = p.q + ((int64_t)seq * R + rt * 16) * kDqk;
-        for (int i = threadIdx.x; i < 16 * (kDqk / 8); i += kThreads) {
+        constexpr int kQPieces = 16 * (kDqk / 8);
+        constexpr int kQPer = (kQPieces + kThreads - 1) / kThreads;
+        u32x4_t qv[kQPer];
+#pragma unroll
+        for (int j = 0; j < kQPer; ++j) {
+            const int i = threadIdx.x + j * kThreads;
             const int qr = i / (kDqk / 8), qc = 8 * (i % (kDqk / 8));
-            *reinterpret_cast<__attribute__((address_space(3))) u32x4_t *>(qs + qr * kQStride + qc) =
-                *reinterpret_cast<const u32x4_t *>(qtile + qr * kDqk + qc);
+            qv[j] = i < kQPieces ? *reinterpret_cast<const u32x4_t *>(qtile + qr * kDqk + qc)
+                                 : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        ChunkRegs ka, kb;
+        load_chunk(ka, p, bt, seq, nc > 0 ? c : c_begin, nc > 0 ? ke : 0, r16, g);
+#pragma unroll
+        for (int j = 0; j < kQPer; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            const int qr = i / (kDqk / 8), qc = 8 * (i % (kDqk / 8));
+            if (i < kQPieces)
+                *reinterpret_cast<__attribute__((address_space(3))) u32x4_t *>(qs + qr * kQStride +
+                                                                               qc) = qv[j];
         }
         __syncthreads();
         const int row = rt * 16 + r16;
@@ -225,15 +250,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_r16_kernel(
 #pragma unroll
         for (int d = 0; d < kDTiles; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        const int c_begin = ks / kChunk;
-        const int c_end = (ke + kChunk - 1) / kChunk;
-        const int mine = c_end - c_begin - wave;
-        const int nc = mine > 0 ? (mine + kWaves - 1) / kWaves : 0;
         MLA_STAMP_PHASE(0);
         if (nc > 0) {
-            ChunkRegs ka, kb;
-            int c = c_begin + wave;
-            load_chunk(ka, p, bt, seq, c, ke, r16, g);
             for (int it = 0;; it += 2) {
                 const int cn = c + kWaves;
                 // always issue the next loads; past the wave's last chunk they
